@@ -305,3 +305,14 @@ def tokens_f64(seed: int, stream: int, row0: int, nrows: int, d: int) -> np.ndar
 # C5: B=100K, lognormal lengths (median 70, clipped 8-512), CSR, Nq=32, d=128, bf16 or PQ codes
 #     (M=16 subspaces of 8 dims, K=256 unit-norm Gaussian centroids).
 SEEDS = {"C1": 1, "C2": 2, "C3": 3, "C4": 4, "C5": 5}
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda"):
+    """Copy a storage array to a torch device tensor of the matching torch dtype
+    (bf16 raw bits are reinterpreted as torch.bfloat16)."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)

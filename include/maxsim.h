@@ -1,0 +1,140 @@
+/*
+ * libmaxsim -- late-interaction MaxSim scoring on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TileMaxSim deep reading, section 1; Flash-MaxSim abstract and
+ * Figure 1): for one query of q_len tokens q_i and each document b of len_b
+ * tokens d_j,
+ *
+ *     out[b] = sum_{i < q_len}  max_{j < len_b}  <q_i, d_j>
+ *
+ * one fp32 score per (query, document) pair. The query-token x document-token
+ * similarity matrix is never written to memory: each document is read from HBM
+ * once, the tile products run on the matrix cores with fp32 accumulation, the
+ * running maxima stay in registers and only the scalar score is stored.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, keeps no per-call state and never reads device memory
+ *    on the host. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and results are valid once that stream has synchronised.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns a negative maxsim_status and enqueues nothing. A call with
+ *    n_docs == 0 returns MAXSIM_OK and enqueues nothing.
+ *  - Contents are not checked: malformed doc_offsets (decreasing, or past the
+ *    token array), NaN or Inf inputs give undefined scores.
+ *  - Storage is row-major and densely packed. Q, D, codes and tables must be
+ *    16-byte aligned; out, scales and offsets naturally aligned.
+ *  - An empty document (length 0) scores -inf (a max over no tokens).
+ *  - Thread-safe; calls on different streams may overlap.
+ */
+#ifndef MAXSIM_H
+#define MAXSIM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats of Q and D for the dense entry points. */
+enum maxsim_dtype {
+  MAXSIM_BF16 = 0, /* bfloat16 */
+  MAXSIM_FP16 = 1, /* IEEE binary16 */
+  MAXSIM_FP32 = 2  /* IEEE binary32; full-precision products (no reduced-precision path) */
+};
+
+enum maxsim_status {
+  MAXSIM_OK = 0,
+  MAXSIM_ERR_NULL = -1,        /* a required pointer is NULL */
+  MAXSIM_ERR_SHAPE = -2,       /* a size is out of range */
+  MAXSIM_ERR_DTYPE = -3,       /* unknown dtype */
+  MAXSIM_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+  MAXSIM_ERR_UNSUPPORTED = -5, /* valid, but no kernel for this combination */
+  MAXSIM_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
+  MAXSIM_ERR_DEVICE = -7       /* no usable gfx950 device is current */
+};
+
+/* Limits checked by every entry point. */
+#define MAXSIM_MAX_Q_LEN 1024 /* query tokens (ColPali-shaped queries: Flash-MaxSim Figure 2) */
+#define MAXSIM_MIN_D 32
+#define MAXSIM_MAX_D 1024 /* d % 32 == 0 (TileMaxSim deep reading, section 2 item (2): d = 64..768) */
+
+/*
+ * Variable-length (padding-free) documents in CSR form (Flash-MaxSim
+ * abstract: variable-length scoring; TileMaxSim deep reading, section 6:
+ * packed documents).
+ *   Q           [q_len][d] in `dtype`, 1 <= q_len <= MAXSIM_MAX_Q_LEN
+ *   D           [doc_offsets[n_docs]][d] in `dtype`: all document tokens, packed
+ *   doc_offsets int64 [n_docs + 1]; document b is tokens [doc_offsets[b], doc_offsets[b+1]);
+ *               doc_offsets[0] is normally 0 and the sequence must not decrease
+ *   d           embedding dimension, a multiple of 32 in [MAXSIM_MIN_D, MAXSIM_MAX_D]
+ *   out         fp32 [n_docs]
+ */
+int maxsim_score(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
+                 int64_t n_docs, int d, int dtype, float *out, void *stream);
+
+/*
+ * Fixed-length documents (TileMaxSim deep reading, section 2: documents of Nd
+ * tokens; section 5: padding to a fixed Nd).
+ *   D        [n_docs][nd][d] in `dtype`, nd >= 1
+ *   doc_lens nullable int32 [n_docs]: valid tokens of each document; tokens
+ *            j >= doc_lens[b] are padding and never affect the score. Values are
+ *            clamped to [0, nd]. NULL means every document has nd valid tokens.
+ *   other arguments as for maxsim_score.
+ */
+int maxsim_score_fixed(const void *Q, int q_len, const void *D, int64_t n_docs, int nd,
+                       const int32_t *doc_lens, int d, int dtype, float *out, void *stream);
+
+/*
+ * INT8 x INT8 scoring with per-token fp32 scales (Flash-MaxSim abstract:
+ * INT8xINT8 quantisation). With dot_ij the exact int32 dot product of the
+ * stored int8 tokens, the scaled similarity is
+ *     v_ij = fl32( fl32(dot_ij) * fl32(q_scale[i] * d_scale[j]) )
+ * (round to nearest even, each product rounded once); out[b] = sum_i max_j v_ij.
+ *   Q        int8 [q_len][d];  q_scale fp32 [q_len]
+ *   D        int8 [tokens][d]; d_scale fp32 [tokens]
+ *   doc_offsets  nullable: CSR as in maxsim_score; NULL means fixed documents of
+ *            nd tokens each (tokens = n_docs * nd)
+ *   d        a multiple of 64 in [64, MAXSIM_MAX_D]
+ *   tok_max  nullable fp32 [n_docs][q_len]: max_j v_ij per query token (bit-exact)
+ *   tok_arg  nullable int32 [n_docs][q_len]: the j attaining it, lowest j on ties,
+ *            -1 for an empty document. tok_max and tok_arg are both NULL or both set.
+ */
+int maxsim_score_i8(const int8_t *Q, const float *q_scale, int q_len, const int8_t *D,
+                    const float *d_scale, const int64_t *doc_offsets, int64_t n_docs, int nd,
+                    int d, float *out, float *tok_max, int32_t *tok_arg, void *stream);
+
+/*
+ * Per-query product-quantisation distance tables (TileMaxSim deep reading,
+ * section 2 item (3)):  T[i][m][k] = sum_{t < dsub} Q[i][m*dsub + t] * C[m][k][t]
+ *   Q  [q_len][M*dsub] in `dtype`
+ *   C  fp32 [M][K][dsub] codebook
+ *   T  fp32 [q_len][M][K] (output, caller-allocated: q_len*M*K*4 bytes)
+ *   Supported: K == 256, M*dsub a multiple of 32 in [MAXSIM_MIN_D, MAXSIM_MAX_D], dsub <= 32.
+ */
+int maxsim_pq_tables(const void *Q, int q_len, int dtype, const float *C, int M, int K, int dsub,
+                     float *T, void *stream);
+
+/*
+ * Fused PQ lookup scoring (TileMaxSim deep reading, section 2 item (3)): token
+ * j's similarity to query token i is sum_m T[i][m][codes[j][m]], then max over
+ * j and sum over i as above. Codes are never decompressed to vectors.
+ *   T      fp32 [q_len][M][K] from maxsim_pq_tables
+ *   codes  uint8 [tokens][M]
+ *   doc_offsets nullable: CSR, or NULL for fixed documents of nd tokens
+ *   Supported: K == 256, M == 16, q_len <= 64.
+ */
+int maxsim_score_pq(const float *T, int q_len, int M, int K, const uint8_t *codes,
+                    const int64_t *doc_offsets, int64_t n_docs, int nd, float *out, void *stream);
+
+/* Static description of a status code. */
+const char *maxsim_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int maxsim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAXSIM_H */

@@ -1,0 +1,33 @@
+/*
+ * Measurement helpers shipped with libmaxsim (not part of the scoring path).
+ *
+ * maxsim_calib_read streams `bytes` from `src` with 128-bit loads and writes one
+ * word per workgroup to `sink` (so the reads cannot be optimised away): its
+ * duration gives the achievable HBM read bandwidth of the device, the ceiling a
+ * memory-bound scoring kernel can approach.
+ * maxsim_calib_copy copies `bytes` from src to dst with 128-bit loads and stores:
+ * a plain copy of known size, used to scale hardware traffic counters.
+ *
+ *   src, dst  device pointers, 16-byte aligned; bytes a multiple of 16
+ *   sink      device fp32/uint32 buffer of at least 65536 words
+ *   stream    hipStream_t (NULL = default stream)
+ * Returns 0 or a negative maxsim_status code (include/maxsim.h).
+ */
+#ifndef MAXSIM_CALIB_H
+#define MAXSIM_CALIB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAXSIM_CALIB_H */

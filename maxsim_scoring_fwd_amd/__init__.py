@@ -1,0 +1,199 @@
+"""MI355X-native late-interaction MaxSim scoring.
+
+Thin Python front end of libmaxsim.so (the C-ABI in include/maxsim.h). The
+functions here only marshal arguments: torch tensors supply device memory and
+the current HIP stream, and every step of the computation runs in the HIP
+kernels of libmaxsim. There is no CPU fallback: if the library is missing or no
+gfx950 device is present, the calls raise.
+
+    score(q_i, d_j) summed:  out[b] = sum_i max_j <q_i, d_j>
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmaxsim.so")
+
+MAXSIM_BF16, MAXSIM_FP16, MAXSIM_FP32 = 0, 1, 2
+_TORCH_DTYPE = {torch.bfloat16: MAXSIM_BF16, torch.float16: MAXSIM_FP16,
+                torch.float32: MAXSIM_FP32}
+
+STATUS = {0: "MAXSIM_OK", -1: "MAXSIM_ERR_NULL", -2: "MAXSIM_ERR_SHAPE", -3: "MAXSIM_ERR_DTYPE",
+          -4: "MAXSIM_ERR_ALIGN", -5: "MAXSIM_ERR_UNSUPPORTED", -6: "MAXSIM_ERR_LAUNCH",
+          -7: "MAXSIM_ERR_DEVICE"}
+
+
+class MaxSimError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmaxsim.so with argument types declared."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python -m maxsim_scoring_fwd_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.maxsim_score.argtypes = [vp, i32, vp, vp, i64, i32, i32, vp, vp]
+        L.maxsim_score_fixed.argtypes = [vp, i32, vp, i64, i32, vp, i32, i32, vp, vp]
+        L.maxsim_score_i8.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp]
+        L.maxsim_pq_tables.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, vp]
+        L.maxsim_score_pq.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp]
+        L.maxsim_status_string.argtypes = [i32]
+        L.maxsim_status_string.restype = ctypes.c_char_p
+        L.maxsim_version.argtypes = []
+        for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
+                  "maxsim_score_pq", "maxsim_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(rc: int, func: str):
+    if rc != 0:
+        raise MaxSimError(rc, func, lib().maxsim_status_string(rc).decode())
+
+
+def _dev(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _TORCH_DTYPE:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _TORCH_DTYPE[t.dtype]
+
+
+def _out(out, n, device, dtype=torch.float32):
+    if out is None:
+        return torch.empty(n, dtype=dtype, device=device)
+    return out
+
+
+def maxsim_score(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """CSR documents. Q [q_len, d], D [n_tokens, d] (same dtype), doc_offsets int64
+    [n_docs+1]; returns fp32 scores [n_docs]."""
+    n_docs = doc_offsets.numel() - 1
+    out = _out(out, n_docs, Q.device)
+    _check(lib().maxsim_score(_dev(Q, "Q"), Q.shape[0], _dev(D, "D"),
+                              _dev(doc_offsets, "doc_offsets"), n_docs, Q.shape[1],
+                              _dtype_code(Q), _dev(out, "out"), _stream(stream)), "maxsim_score")
+    return out
+
+
+def maxsim_score_fixed(Q: torch.Tensor, D: torch.Tensor, doc_lens: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fixed-length documents. Q [q_len, d], D [n_docs, nd, d]; doc_lens int32 [n_docs]
+    (optional) masks trailing padding tokens. Returns fp32 scores [n_docs]."""
+    if D.dtype != Q.dtype:
+        raise ValueError("Q and D must share a dtype")
+    n_docs, nd = D.shape[0], D.shape[1]
+    out = _out(out, n_docs, Q.device)
+    _check(lib().maxsim_score_fixed(_dev(Q, "Q"), Q.shape[0], _dev(D, "D"), n_docs, nd,
+                                    _dev(doc_lens, "doc_lens"), Q.shape[1], _dtype_code(Q),
+                                    _dev(out, "out"), _stream(stream)), "maxsim_score_fixed")
+    return out
+
+
+def maxsim_score_i8(Q: torch.Tensor, q_scale: torch.Tensor, D: torch.Tensor,
+                    d_scale: torch.Tensor, doc_offsets: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, with_token_max: bool = False, stream=None):
+    """INT8 x INT8 with per-token fp32 scales. Fixed layout (D [n_docs, nd, d]) when
+    doc_offsets is None, else CSR (D [n_tokens, d]). Returns scores, or (scores, tok_max,
+    tok_arg) with with_token_max."""
+    q_len, d = Q.shape
+    if doc_offsets is None:
+        n_docs, nd = D.shape[0], D.shape[1]
+    else:
+        n_docs, nd = doc_offsets.numel() - 1, 0
+    out = _out(out, n_docs, Q.device)
+    tm = ta = None
+    if with_token_max:
+        tm = torch.empty((n_docs, q_len), dtype=torch.float32, device=Q.device)
+        ta = torch.empty((n_docs, q_len), dtype=torch.int32, device=Q.device)
+    _check(lib().maxsim_score_i8(_dev(Q, "Q"), _dev(q_scale, "q_scale"), q_len, _dev(D, "D"),
+                                 _dev(d_scale, "d_scale"), _dev(doc_offsets, "doc_offsets"),
+                                 n_docs, nd, d, _dev(out, "out"), _dev(tm, "tok_max"),
+                                 _dev(ta, "tok_arg"), _stream(stream)), "maxsim_score_i8")
+    return (out, tm, ta) if with_token_max else out
+
+
+def maxsim_pq_tables(Q: torch.Tensor, C: torch.Tensor, T: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """PQ distance tables T [q_len, M, K] fp32 from Q [q_len, M*dsub] and C [M, K, dsub] fp32."""
+    M, K, dsub = C.shape
+    if T is None:
+        T = torch.empty((Q.shape[0], M, K), dtype=torch.float32, device=Q.device)
+    _check(lib().maxsim_pq_tables(_dev(Q, "Q"), Q.shape[0], _dtype_code(Q), _dev(C, "C"), M, K,
+                                  dsub, _dev(T, "T"), _stream(stream)), "maxsim_pq_tables")
+    return T
+
+
+def maxsim_score_pq(T: torch.Tensor, codes: torch.Tensor, doc_offsets: torch.Tensor | None = None,
+                    nd: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fused PQ lookup scoring. T [q_len, M, K] fp32, codes uint8 [n_tokens, M]; CSR when
+    doc_offsets is given, else fixed documents of nd tokens."""
+    q_len, M, K = T.shape
+    n_docs = doc_offsets.numel() - 1 if doc_offsets is not None else codes.shape[0] // max(nd, 1)
+    out = _out(out, n_docs, T.device)
+    _check(lib().maxsim_score_pq(_dev(T, "T"), q_len, M, K, _dev(codes, "codes"),
+                                 _dev(doc_offsets, "doc_offsets"), n_docs, nd, _dev(out, "out"),
+                                 _stream(stream)), "maxsim_score_pq")
+    return out
+
+
+def version() -> int:
+    return lib().maxsim_version()
+
+
+# ---- measurement helpers (include/maxsim_calib.h) ----
+
+def _calib_lib():
+    L = lib()
+    if not getattr(L, "_calib_bound", False):
+        vp = ctypes.c_void_p
+        L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.maxsim_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.maxsim_calib_read.restype = ctypes.c_int
+        L.maxsim_calib_copy.restype = ctypes.c_int
+        L._calib_bound = True
+    return L
+
+
+def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream-read every byte of src (achievable read bandwidth); sink: >= 65536 words."""
+    _check(_calib_lib().maxsim_calib_read(_dev(src, "src"), src.numel() * src.element_size(),
+                                          _dev(sink, "sink"), _stream(stream)), "maxsim_calib_read")
+
+
+def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Plain 128-bit copy of src into dst (known traffic for counter scaling)."""
+    _check(_calib_lib().maxsim_calib_copy(_dev(src, "src"), _dev(dst, "dst"),
+                                          src.numel() * src.element_size(), _stream(stream)),
+           "maxsim_calib_copy")

@@ -1,0 +1,17 @@
+// Dense kernel dispatch: one translation unit per storage type instantiates the
+// (chunks per d block, query blocks, pipeline depth, Q placement) variants.
+#pragma once
+
+#include "dense_kernel.hpp"
+#include "host_common.hpp"
+
+namespace maxsim {
+
+int dense_dispatch_bf16(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                        const DeviceInfo &di, hipStream_t st);
+int dense_dispatch_fp16(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                        const DeviceInfo &di, hipStream_t st);
+int dense_dispatch_fp32(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                        const DeviceInfo &di, hipStream_t st);
+
+}  // namespace maxsim

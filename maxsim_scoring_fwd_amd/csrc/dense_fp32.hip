@@ -1,0 +1,11 @@
+// Dense MaxSim kernels for fp32 storage.
+#include "dense_variants.hpp"
+
+namespace maxsim {
+
+int dense_dispatch_fp32(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                        const DeviceInfo &di, hipStream_t st) {
+  return dense_by_mode<DT_FP32>(qlds, ksb, qb, a, lds, di, st);
+}
+
+}  // namespace maxsim

@@ -1,0 +1,146 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects bad
+arguments with the documented status codes before touching the GPU (CPU-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import maxsim_scoring_fwd_amd as ms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maxsim.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ms.LIB_PATH):
+        from maxsim_scoring_fwd_amd import build
+        build.build()
+    return ms.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(maxsim_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
+              "maxsim_score_pq", "maxsim_status_string", "maxsim_version"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {ms.LIB_PATH}").read()
+    exported = set(re.findall(r" T (maxsim_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_no_torch_in_signatures():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("caller-allocated", "")
+    assert "at::" not in text and "Tensor" not in text
+
+
+def test_status_strings_and_version(L):
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, LAUNCH, DEVICE):
+        assert len(L.maxsim_status_string(s)) >= 2
+    assert L.maxsim_version() >= 100
+
+
+def score(L, Q=P, q_len=32, D=P, off=P, n=10, d=128, dt=0, out=P):
+    return L.maxsim_score(Q, q_len, D, off, n, d, dt, out, None)
+
+
+def fixed(L, Q=P, q_len=32, D=P, n=10, nd=128, lens=None, d=128, dt=0, out=P):
+    return L.maxsim_score_fixed(Q, q_len, D, n, nd, lens, d, dt, out, None)
+
+
+def test_dense_argument_errors(L):
+    assert score(L, Q=None) == NULL
+    assert score(L, D=None) == NULL
+    assert score(L, out=None) == NULL
+    assert score(L, off=None) == NULL
+    assert score(L, q_len=0) == SHAPE
+    assert score(L, q_len=1025) == SHAPE
+    assert score(L, d=48) == SHAPE
+    assert score(L, d=16) == SHAPE
+    assert score(L, d=1056) == SHAPE
+    assert score(L, n=-1) == SHAPE
+    assert score(L, dt=3) == DTYPE
+    assert score(L, dt=-1) == DTYPE
+    assert score(L, Q=P + 2) == ALIGN
+    assert score(L, D=P + 8) == ALIGN
+    assert score(L, out=P + 2) == ALIGN
+    assert score(L, off=P + 4) == ALIGN
+    assert fixed(L, nd=0) == SHAPE
+    assert fixed(L, lens=P + 2) == ALIGN
+    assert fixed(L, Q=None) == NULL
+
+
+def test_zero_docs_is_a_no_op(L):
+    assert score(L, n=0) == OK
+    assert fixed(L, n=0) == OK
+    assert L.maxsim_score_i8(P, P, 32, P, P, None, 0, 16, 128, P, None, None, None) == OK
+    assert L.maxsim_score_pq(P, 32, 16, 256, P, None, 0, 16, P, None) == OK
+
+
+def test_i8_argument_errors(L):
+    f = lambda **k: L.maxsim_score_i8(k.get("Q", P), k.get("qs", P), k.get("q_len", 32),
+                                      k.get("D", P), k.get("ds", P), k.get("off", None),
+                                      k.get("n", 5), k.get("nd", 16), k.get("d", 128),
+                                      k.get("out", P), k.get("tm", None), k.get("ta", None), None)
+    assert f(d=96) == SHAPE
+    assert f(d=32) == SHAPE
+    assert f(nd=0) == SHAPE
+    assert f(q_len=0) == SHAPE
+    assert f(Q=None) == NULL
+    assert f(qs=None) == NULL
+    assert f(ds=None) == NULL
+    assert f(tm=P) == NULL  # tok_max without tok_arg
+    assert f(D=P + 4) == ALIGN
+    assert f(qs=P + 1) == ALIGN
+    assert f(off=P + 4) == ALIGN
+
+
+def test_pq_argument_errors(L):
+    t = lambda **k: L.maxsim_pq_tables(k.get("Q", P), k.get("q_len", 32), k.get("dt", 0),
+                                       k.get("C", P), k.get("M", 16), k.get("K", 256),
+                                       k.get("dsub", 8), k.get("T", P), None)
+    assert t(K=128) == UNSUP
+    assert t(dt=7) == DTYPE
+    assert t(M=3, dsub=8) == SHAPE  # d = 24
+    assert t(dsub=33) == SHAPE
+    assert t(C=None) == NULL
+    assert t(T=P + 4) == ALIGN
+    s = lambda **k: L.maxsim_score_pq(k.get("T", P), k.get("q_len", 32), k.get("M", 16),
+                                      k.get("K", 256), k.get("codes", P), k.get("off", None),
+                                      k.get("n", 5), k.get("nd", 16), k.get("out", P), None)
+    assert s(K=16) == UNSUP
+    assert s(M=8) == UNSUP
+    assert s(q_len=65) == UNSUP
+    assert s(nd=0) == SHAPE
+    assert s(codes=None) == NULL
+    assert s(codes=P + 8) == ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+def test_valid_call_without_gpu_reports_device_error(L):
+    assert score(L) == DEVICE
+    assert fixed(L) == DEVICE
+
+
+def test_python_binding_refuses_host_tensors(L):
+    Q = torch.zeros(32, 128, dtype=torch.bfloat16)
+    D = torch.zeros(4, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ms.maxsim_score_fixed(Q, D, out=torch.zeros(4))
