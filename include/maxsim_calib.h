@@ -1,7 +1,8 @@
 /*
  * Measurement helpers shipped with libmaxsim (not part of the scoring path).
  *
- * maxsim_calib_read streams `bytes` from `src` with 128-bit loads and writes one
+ * maxsim_calib_read streams `bytes` from `src` with non-temporal 128-bit loads (each
+ * wave reading whole 16 KiB blocks) and writes one
  * word per workgroup to `sink` (so the reads cannot be optimised away): its
  * duration gives the achievable HBM read bandwidth of the device, the ceiling a
  * memory-bound scoring kernel can approach.

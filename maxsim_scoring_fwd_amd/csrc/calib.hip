@@ -16,6 +16,7 @@ constexpr int CAL_THREADS = 256;
 constexpr int CAL_LOADS = 16;
 constexpr size_t CAL_BLOCK16 = 64 * CAL_LOADS;  // 16-byte pieces per block
 
+template <bool NT>
 __global__ void __launch_bounds__(CAL_THREADS) calib_read_kernel(const u32x4_t *src, size_t n16,
                                                                  uint32_t *sink) {
   const int lane = threadIdx.x & 63;
@@ -27,7 +28,7 @@ __global__ void __launch_bounds__(CAL_THREADS) calib_read_kernel(const u32x4_t *
     const u32x4_t *p = src + b * CAL_BLOCK16 + lane;
     u32x4_t v[CAL_LOADS];
 #pragma unroll
-    for (int u = 0; u < CAL_LOADS; u++) v[u] = p[u * 64];
+    for (int u = 0; u < CAL_LOADS; u++) v[u] = NT ? __builtin_nontemporal_load(p + u * 64) : p[u * 64];
 #pragma unroll
     for (int u = 0; u < CAL_LOADS; u++) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -55,9 +56,11 @@ extern "C" int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, 
   maxsim::DeviceInfo di;
   int rc = maxsim::current_device(di);
   if (rc != MAXSIM_OK) return rc;
-  const int bpc = maxsim::blocks_per_cu((const void *)calib_read_kernel, CAL_THREADS, 0);
-  hipLaunchKernelGGL(calib_read_kernel, dim3(bpc * di.cus), dim3(CAL_THREADS), 0,
-                     (hipStream_t)stream, (const u32x4_t *)src, bytes / 16, sink);
+  static const int nt = maxsim::env_knob("MAXSIM_CALIB_NT", 1);
+  auto kern = nt ? calib_read_kernel<true> : calib_read_kernel<false>;
+  const int bpc = maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
+  hipLaunchKernelGGL(kern, dim3(bpc * di.cus), dim3(CAL_THREADS), 0, (hipStream_t)stream,
+                     (const u32x4_t *)src, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 

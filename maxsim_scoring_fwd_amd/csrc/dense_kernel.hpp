@@ -14,12 +14,18 @@
 //    once. Up to 32 query tokens with d <= 256 live in VGPRs as ready-made MFMA
 //    B operands; wider d keeps Q in LDS with a padded row stride (bank-conflict
 //    free 128-bit reads).
-//  * Document tiles are 16 tokens. Each lane loads 16-byte pieces of one token
-//    row straight into the MFMA A-operand registers (no LDS round trip: each
-//    element is used by exactly one lane, so staging through LDS would only add
-//    traffic). A P-slot register ring keeps P tiles of loads in flight per wave;
-//    every slot always issues its loads (a dummy in-bounds address once the
-//    work is exhausted) so the compiler's vmcnt waits stay uniform.
+//  * Document tiles are 16 tokens. A P-slot register ring keeps P tiles of
+//    loads in flight per wave; every slot always issues its loads (a dummy
+//    in-bounds address once the work is exhausted) so the compiler's vmcnt
+//    waits stay uniform. Two ways to bring a tile to the matrix core:
+//      - staged (default where the row is a power-of-two number of 16-byte
+//        pieces): every load instruction reads 1 KiB of contiguous memory,
+//        marked non-temporal since each byte is read once; the tile is then
+//        transposed through a per-wave LDS buffer (XOR-swizzled, conflict-free)
+//        into MFMA operand layout. Whole cache lines per instruction is what
+//        lets streaming reads approach the HBM ceiling.
+//      - direct: each lane loads its 16-byte pieces of one token row straight
+//        into the MFMA A-operand registers (16 rows x 64 B per instruction).
 //  * The embedding dimension is processed in blocks of KSB*64 bytes; partial
 //    dot products accumulate in the fp32 accumulator across blocks before the
 //    max (TileMaxSim section 2 item (2), dimension tiling).
@@ -49,40 +55,76 @@ struct DenseArgs {
 };
 
 constexpr int DENSE_THREADS = 256;
+constexpr int DENSE_WAVES = DENSE_THREADS / WAVE;
 
-// Extent of document b: first token row and length (wave-uniform).
+// How document tiles reach the matrix core.
+enum { LOAD_DIRECT = 0, LOAD_DIRECT_NT = 1, LOAD_STAGED = 2 };
+
+// Bytes of the per-wave LDS transpose buffer (one 16-token tile of one d block).
+template <int KSB> constexpr int stage_tile_bytes() { return 16 * KSB * 64; }
+
+// LDS piece swizzle of a staged tile with PPR 16-byte pieces per row: rows
+// 0..15 reading the same logical piece land on 16 distinct 16-byte bank groups.
+template <int PPR> __device__ __forceinline__ int stage_swizzle(int row) {
+  if constexpr (PPR >= 16)
+    return row & 15;
+  else
+    return (row * PPR / 16) & (PPR - 1);
+}
+
+// Extent of document b: first token row and length (wave-uniform). The offsets
+// and lengths are read through the constant address space so that they become
+// scalar loads: a vector load here would make every wait on the tile loads in
+// flight also wait for this one (vector loads complete in order).
+typedef __attribute__((address_space(4))) const int64_t c_i64;
+typedef __attribute__((address_space(4))) const int32_t c_i32;
 __device__ __forceinline__ void doc_extent(const DenseArgs &a, int64_t b, int64_t &first,
                                            int64_t &len) {
   if (a.offsets) {
-    first = uniform(a.offsets[b]);
-    len = uniform(a.offsets[b + 1]) - first;
+    const c_i64 *off = (const c_i64 *)a.offsets;
+    first = uniform(off[b]);
+    len = uniform(off[b + 1]) - first;
   } else {
     first = b * (int64_t)a.nd;
     len = a.nd;
     if (a.doc_lens) {
-      int64_t l = uniform(a.doc_lens[b]);
+      int64_t l = uniform((int64_t)((const c_i32 *)a.doc_lens)[b]);
       len = l < 0 ? 0 : (l > a.nd ? a.nd : l);
     }
   }
 }
 
+// Per-slot state of the load ring (wave-uniform). The flags are kept as separate
+// booleans: packed into one integer they lead the compiler to wait for every
+// load in flight before each tile, which serialises the ring.
+struct Slot {
+  int64_t doc;
+  int dblk;
+  bool valid, first_blk, last_blk, doc_end, empty;
+};
+
 // DT: storage type; KSB: 64-byte chunks per d block; QB: 16-query blocks;
-// P: tiles in flight per wave; QLDS: query operand read from LDS.
-template <int DT, int KSB, int QB, int P, bool QLDS>
+// P: tiles in flight per wave; QLDS: query operand read from LDS; LM: load mode.
+template <int DT, int KSB, int QB, int P, bool QLDS, int LM>
 __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds_q[];
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int PPR = KSB * 4;  // 16-byte pieces per row of one d block
+  static_assert(LM != LOAD_STAGED || (PPR & (PPR - 1)) == 0, "staged tiles need 2^k pieces");
   const int lane = threadIdx.x & (WAVE - 1);
   const int r16 = lane & 15;  // tile row (document token) / query column
   const int g = lane >> 4;    // 16-byte piece within a 64-byte chunk
-  const int64_t wave = uniform((int64_t)blockIdx.x * (DENSE_THREADS / WAVE) + (threadIdx.x >> 6));
-  const int64_t nwaves = (int64_t)gridDim.x * (DENSE_THREADS / WAVE);
+  const int wave_in_wg = threadIdx.x >> 6;
+  const int64_t wave = uniform((int64_t)blockIdx.x * DENSE_WAVES + wave_in_wg);
+  const int64_t nwaves = (int64_t)gridDim.x * DENSE_WAVES;
   const int n_dblk = QLDS ? a.n_dblk : 1;
   const int64_t RB = (int64_t)n_dblk * KSB * 64;  // bytes per token row
   const int q_len = a.q_len;
+  const int64_t QROWB = RB + 16;  // padded LDS row stride of Q: 16 rows hit distinct banks
+  const int64_t q_lds_bytes = QLDS ? (int64_t)QB * 16 * QROWB : 0;
+  char *tile = lds + q_lds_bytes + wave_in_wg * stage_tile_bytes<KSB>();
 
   // ---- query tokens, resident for the whole kernel ----
   u32x4_t qreg[QLDS ? 1 : QB][QLDS ? 1 : KSB];
-  const int64_t QROWB = RB + 16;  // padded LDS row stride: 16 rows hit distinct banks
   if constexpr (!QLDS) {
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
@@ -101,63 +143,76 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       const int64_t row = idx / per_row, col = idx - row * per_row;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (row < q_len) v = load16(a.Q + row * RB + col * 16);
-      *reinterpret_cast<u32x4_t *>(lds_q + row * QROWB + col * 16) = v;
+      *reinterpret_cast<u32x4_t *>(lds + row * QROWB + col * 16) = v;
     }
     __syncthreads();
   }
 
   // ---- producer: the (doc, tile, d-block) sequence of this wave ----
+  // No loops and no stores here: an empty document becomes one slot flagged
+  // SLOT_EMPTY whose score (-inf, a max over no tokens) the consumer writes.
   int64_t pb = wave, pfirst = 0, plen = 0, ptile = 0;
   int pk = 0;
-  auto next_doc = [&](int64_t b) {
-    // Skip empty documents (score -inf: a max over no tokens).
-    while (b < a.n_docs) {
-      doc_extent(a, b, pfirst, plen);
-      if (plen > 0) break;
-      if (lane == 0) a.out[b] = -__builtin_inff();
-      b += nwaves;
-    }
-    pb = b;
-    ptile = 0;
-    pk = 0;
-  };
-  next_doc(pb);
+  if (pb < a.n_docs) doc_extent(a, pb, pfirst, plen);
 
   u32x4_t buf[P][KSB];
-  bool s_valid[P];
-  int64_t s_doc[P];
-  int s_dblk[P];
-  bool s_first[P], s_last_blk[P], s_doc_end[P];
+  Slot slot[P];
 
-  auto issue = [&](u32x4_t(&dst)[KSB], bool &valid, int64_t &doc, int &dblk, bool &first_blk,
-                   bool &last_blk, bool &doc_end) {
-    valid = pb < a.n_docs;
-    const char *base = a.Q;
-    int64_t lane_off = g * 16;
-    if (valid) {
-      const int64_t t0 = ptile * 16;
-      int64_t row = plen - 1 - t0;
-      row = row < r16 ? row : r16;
-      base = a.D + (pfirst + t0) * RB + (int64_t)pk * KSB * 64;
-      lane_off = row * RB + g * 16;
-      doc = pb;
-      dblk = pk;
-      first_blk = (pk == 0);
-      last_blk = (pk == n_dblk - 1);
-      const int64_t ntiles = (plen + 15) >> 4;
-      doc_end = last_blk && (ptile == ntiles - 1);
-      if (++pk == n_dblk) {
+  auto issue = [&](u32x4_t(&dst)[KSB], Slot &sl) {
+    sl.valid = false;
+    const char *base = a.Q;  // in-bounds dummy source for empty or exhausted slots
+    int last = 0;            // last valid row of the tile
+    if (pb < a.n_docs) {
+      sl.valid = true;
+      sl.doc = pb;
+      bool advance = true;
+      if (plen == 0) {
+        sl.dblk = 0;
+        sl.first_blk = sl.last_blk = sl.doc_end = sl.empty = true;
+      } else {
+        const int64_t t0 = ptile * 16;
+        const int64_t rem = plen - 1 - t0;
+        last = rem < 15 ? (int)rem : 15;
+        base = a.D + (pfirst + t0) * RB + (int64_t)pk * KSB * 64;
+        const int64_t ntiles = (plen + 15) >> 4;
+        sl.dblk = pk;
+        sl.empty = false;
+        sl.first_blk = (pk == 0);
+        sl.last_blk = (pk == n_dblk - 1);
+        sl.doc_end = sl.last_blk && (ptile == ntiles - 1);
+        advance = false;
+        if (++pk == n_dblk) {
+          pk = 0;
+          if (++ptile == ntiles) advance = true;
+        }
+      }
+      if (advance) {
+        pb += nwaves;
+        ptile = 0;
         pk = 0;
-        if (++ptile == ntiles) next_doc(pb + nwaves);
+        if (pb < a.n_docs) doc_extent(a, pb, pfirst, plen);
       }
     }
+    // The same per-lane formula serves the dummy case (base = Q, last = 0: every lane
+    // reads within the first query row), so only wave-uniform values differ.
+    if constexpr (LM == LOAD_STAGED) {
 #pragma unroll
-    for (int c = 0; c < KSB; c++) dst[c] = load16(base + lane_off + c * 64);
+      for (int c = 0; c < KSB; c++) {
+        const int u = c * 64 + lane;  // linear 16-byte piece of the tile
+        const int row = u / PPR < last ? u / PPR : last;
+        dst[c] = load16_nt(base + (int64_t)row * RB + (u % PPR) * 16);
+      }
+    } else {
+      const int row = r16 < last ? r16 : last;
+      const int64_t off = (int64_t)row * RB + g * 16;
+#pragma unroll
+      for (int c = 0; c < KSB; c++)
+        dst[c] = LM == LOAD_DIRECT_NT ? load16_nt(base + off + c * 64) : load16(base + off + c * 64);
+    }
   };
 
 #pragma unroll
-  for (int p = 0; p < P; p++)
-    issue(buf[p], s_valid[p], s_doc[p], s_dblk[p], s_first[p], s_last_blk[p], s_doc_end[p]);
+  for (int p = 0; p < P; p++) issue(buf[p], slot[p]);
 
   f32x4_t acc[QB];
   float m[QB];
@@ -170,8 +225,25 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
   for (;;) {
 #pragma unroll
     for (int p = 0; p < P; p++) {
-      if (!s_valid[p]) goto done;
-      if (s_first[p]) {
+      if (!slot[p].valid) goto done;
+      u32x4_t aop[KSB];
+      if constexpr (LM == LOAD_STAGED) {
+        // transpose through LDS: linear pieces in, one token row per lane out
+#pragma unroll
+        for (int c = 0; c < KSB; c++) {
+          const int u = c * 64 + lane, row = u / PPR, piece = u % PPR;
+          *reinterpret_cast<u32x4_t *>(tile + (row * PPR + (piece ^ stage_swizzle<PPR>(row))) * 16) =
+              buf[p][c];
+        }
+#pragma unroll
+        for (int c = 0; c < KSB; c++)
+          aop[c] = *reinterpret_cast<const u32x4_t *>(
+              tile + (r16 * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(r16))) * 16);
+      } else {
+#pragma unroll
+        for (int c = 0; c < KSB; c++) aop[c] = buf[p][c];
+      }
+      if (slot[p].first_blk) {
 #pragma unroll
         for (int qb = 0; qb < QB; qb++) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
@@ -182,17 +254,17 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
           u32x4_t qv;
           if constexpr (QLDS)
             qv = *reinterpret_cast<const u32x4_t *>(
-                lds_q + (qb * 16 + r16) * QROWB + ((int64_t)s_dblk[p] * KSB + c) * 64 + g * 16);
+                lds + (qb * 16 + r16) * QROWB + ((int64_t)slot[p].dblk * KSB + c) * 64 + g * 16);
           else
             qv = qreg[qb][c];
-          acc[qb] = ChunkMfma<DT>::run(buf[p][c], qv, acc[qb]);
+          acc[qb] = ChunkMfma<DT>::run(aop[c], qv, acc[qb]);
         }
       }
-      if (s_last_blk[p]) {
+      if (slot[p].last_blk) {
 #pragma unroll
         for (int qb = 0; qb < QB; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
       }
-      if (s_doc_end[p]) {
+      if (slot[p].doc_end) {
         float s = 0.f;
 #pragma unroll
         for (int qb = 0; qb < QB; qb++) {
@@ -206,9 +278,10 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
         s += __shfl_xor(s, 8);
-        if (lane == 0) a.out[s_doc[p]] = s;
+        if (slot[p].empty) s = -__builtin_inff();
+        if (lane == 0) a.out[slot[p].doc] = s;
       }
-      issue(buf[p], s_valid[p], s_doc[p], s_dblk[p], s_first[p], s_last_blk[p], s_doc_end[p]);
+      issue(buf[p], slot[p]);
     }
   }
 done:

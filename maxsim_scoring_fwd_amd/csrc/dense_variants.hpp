@@ -6,33 +6,48 @@
 namespace maxsim {
 namespace {
 
-constexpr int DENSE_WAVES_PER_WG = DENSE_THREADS / WAVE;
-
-template <int DT, int KSB, int QB, int P, bool QLDS>
-int launch_dense(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipStream_t st) {
-  auto kern = dense_maxsim_kernel<DT, KSB, QB, P, QLDS>;
+template <int DT, int KSB, int QB, int P, bool QLDS, int LM>
+int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStream_t st) {
+  auto kern = dense_maxsim_kernel<DT, KSB, QB, P, QLDS, LM>;
+  const size_t lds = q_lds + (LM == LOAD_STAGED ? DENSE_WAVES * stage_tile_bytes<KSB>() : 0);
+  if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
   const int bpc = blocks_per_cu((const void *)kern, DENSE_THREADS, lds);
   const int64_t max_wg = (int64_t)bpc * di.cus;
-  const int64_t need = (a.n_docs + DENSE_WAVES_PER_WG - 1) / DENSE_WAVES_PER_WG;
+  const int64_t need = (a.n_docs + DENSE_WAVES - 1) / DENSE_WAVES;
   int64_t grid = need < max_wg ? need : max_wg;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(DENSE_THREADS), lds, st, a);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
-// Tiles in flight per wave: about 32 KiB of loads per wave for small chunks counts.
+// Staged loads need a power-of-two number of 16-byte pieces per row.
+template <int KSB> constexpr bool stageable() { return (KSB & (KSB - 1)) == 0; }
+
+// Tiles in flight per wave: about 32 KiB of loads per wave.
 template <int KSB> constexpr int default_depth() { return KSB <= 4 ? 8 : 4; }
 
 template <int DT, int KSB, int QB, bool QLDS>
 int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipStream_t st) {
+  constexpr int LM = stageable<KSB>() ? LOAD_STAGED : LOAD_DIRECT;
   if constexpr (DT == DT_BF16 && KSB == 4 && QB == 2 && !QLDS) {
-    // The ColBERT shape (d = 128, 32 query tokens): depth selectable for measurements.
+    // The ColBERT shape (d = 128, 32 query tokens): load mode and depth selectable
+    // for measurements.
     static const int depth = env_knob("MAXSIM_DENSE_DEPTH", 0);
-    if (depth == 2) return launch_dense<DT, KSB, QB, 2, QLDS>(a, lds, di, st);
-    if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS>(a, lds, di, st);
-    if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS>(a, lds, di, st);
+    static const int mode = env_knob("MAXSIM_DENSE_LOAD", LM);
+    if (mode == LOAD_DIRECT) {
+      if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_DIRECT>(a, lds, di, st);
+      return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT>(a, lds, di, st);
+    }
+    if (mode == LOAD_DIRECT_NT) return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT_NT>(a, lds, di, st);
+    if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LOAD_STAGED>(a, lds, di, st);
+    if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED>(a, lds, di, st);
   }
-  return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS>(a, lds, di, st);
+  if constexpr (LM == LOAD_STAGED) {
+    // Where Q already fills LDS, the transpose buffers may not fit: load directly.
+    if (lds + DENSE_WAVES * stage_tile_bytes<KSB>() > di.max_lds)
+      return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LOAD_DIRECT>(a, lds, di, st);
+  }
+  return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LM>(a, lds, di, st);
 }
 
 template <int DT, int KSB, bool QLDS>

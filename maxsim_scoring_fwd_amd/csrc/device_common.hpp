@@ -76,6 +76,11 @@ __device__ __forceinline__ u32x4_t load16(const char *p) {
   return *reinterpret_cast<const u32x4_t *>(p);
 }
 
+// Streaming load: the data is read exactly once, so it is marked non-temporal.
+__device__ __forceinline__ u32x4_t load16_nt(const char *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
 __device__ __forceinline__ float max4(f32x4_t v) {
   return __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
 }
