@@ -69,6 +69,10 @@ enum maxsim_status {
  *               doc_offsets[0] is normally 0 and the sequence must not decrease
  *   d           embedding dimension, a multiple of 32 in [MAXSIM_MIN_D, MAXSIM_MAX_D]
  *   out         fp32 [n_docs]
+ * Up to 64 query tokens are scored by one wave per document with the whole query
+ * resident; longer queries (up to 1024, Flash-MaxSim Figure 2: Lq = 1024) are split
+ * across the waves of a workgroup and need d * element bytes to be 64, 128, 256 or
+ * 512 bytes and q_len <= 1024 * 64 / (d * element bytes), else MAXSIM_ERR_UNSUPPORTED.
  */
 int maxsim_score(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
                  int64_t n_docs, int d, int dtype, float *out, void *stream);
@@ -95,7 +99,7 @@ int maxsim_score_fixed(const void *Q, int q_len, const void *D, int64_t n_docs, 
  *   D        int8 [tokens][d]; d_scale fp32 [tokens]
  *   doc_offsets  nullable: CSR as in maxsim_score; NULL means fixed documents of
  *            nd tokens each (tokens = n_docs * nd)
- *   d        a multiple of 64 in [64, MAXSIM_MAX_D]
+ *   d        64, 128, 256 or 512 (other multiples of 64 return MAXSIM_ERR_UNSUPPORTED)
  *   tok_max  nullable fp32 [n_docs][q_len]: max_j v_ij per query token (bit-exact)
  *   tok_arg  nullable int32 [n_docs][q_len]: the j attaining it, lowest j on ties,
  *            -1 for an empty document. tok_max and tok_arg are both NULL or both set.

@@ -5,11 +5,10 @@
 // caller's stream. Nothing here reads device memory or allocates.
 #include <hip/hip_runtime.h>
 
-#include "bigq_kernel.hpp"
 #include "dense_dispatch.hpp"
 #include "dense_kernel.hpp"
 #include "host_common.hpp"
-#include "i8_kernel.hpp"
+#include "tiled_dispatch.hpp"
 #include "pq_kernel.hpp"
 
 using namespace maxsim;
@@ -25,7 +24,12 @@ int dense_run(DenseArgs a, int d, int dtype, hipStream_t st) {
   const int chunks = d * eb / 64;          // 64-byte pieces per token row
   const int qb = (a.q_len + 15) / 16;      // 16-query blocks
   static const int force_lds = env_knob("MAXSIM_DENSE_QLDS", 0);
-  if (qb > 4) return dense_big_q_run(a, d, dtype, di, st);
+  if (qb > 4) {
+    // Long queries: query slices across the waves of a workgroup.
+    TiledArgs t{a.Q, a.q_len, a.D, a.offsets, a.n_docs, a.nd, a.doc_lens, nullptr, nullptr,
+                a.out, nullptr, nullptr};
+    return tiled_dense_run(t, d, dtype, di, st);
+  }
   bool qlds = force_lds || chunks > 8 || chunks * qb > 16;
   int ksb = chunks;
   if (qlds) {
@@ -85,8 +89,9 @@ int maxsim_score_i8(const int8_t *Q, const float *q_scale, int q_len, const int8
   DeviceInfo di;
   int rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
-  I8Args a{Q, q_scale, q_len, D, d_scale, doc_offsets, n_docs, nd, d, out, tok_max, tok_arg};
-  return i8_run(a, di, (hipStream_t)stream);
+  TiledArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs, nd, nullptr, q_scale,
+              d_scale, out, tok_max, tok_arg};
+  return tiled_i8_run(a, d, di, (hipStream_t)stream);
 }
 
 int maxsim_pq_tables(const void *Q, int q_len, int dtype, const float *C, int M, int K, int dsub,

@@ -1,0 +1,63 @@
+// Launch of the query-tiled kernel (long queries and INT8).
+#pragma once
+
+#include "host_common.hpp"
+#include "tiled_kernel.hpp"
+
+namespace maxsim {
+
+// Query blocks per wave for a query length (8 waves x 16 tokens x QBW >= q_len).
+inline int tiled_qbw(int q_len) { return (q_len + TILED_WAVES * 16 - 1) / (TILED_WAVES * 16); }
+
+// Largest query length the tiled kernel holds for KSB 64-byte chunks per row:
+// the slice of one wave needs QBW * KSB * 4 VGPRs, kept at or below 128.
+inline int tiled_max_q(int ksb) { return TILED_WAVES * 16 * (32 / ksb > 16 ? 16 : 32 / ksb); }
+
+template <int DT, int KSB, int QBW, bool ARG>
+int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
+  auto kern = tiled_maxsim_kernel<DT, KSB, QBW, ARG>;
+  const int bpc = blocks_per_cu((const void *)kern, TILED_THREADS, 0);
+  const int64_t max_wg = (int64_t)bpc * di.cus;
+  int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TILED_THREADS), 0, st, a);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+template <int DT, int KSB, bool ARG>
+int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
+  switch (qbw) {
+#define MAXSIM_TILED_CASE(N)                                                                      \
+  case N:                                                                                         \
+    if constexpr (N * KSB <= 32) return launch_tiled<DT, KSB, N, ARG>(a, di, st);                 \
+    break;
+    MAXSIM_TILED_CASE(1)
+    MAXSIM_TILED_CASE(2)
+    MAXSIM_TILED_CASE(3)
+    MAXSIM_TILED_CASE(4)
+    MAXSIM_TILED_CASE(5)
+    MAXSIM_TILED_CASE(6)
+    MAXSIM_TILED_CASE(7)
+    MAXSIM_TILED_CASE(8)
+#undef MAXSIM_TILED_CASE
+  }
+  return MAXSIM_ERR_UNSUPPORTED;
+}
+
+template <int DT, bool ARG>
+int tiled_by_ksb(int ksb, int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
+  switch (ksb) {
+  case 1: return tiled_by_qbw<DT, 1, ARG>(qbw, a, di, st);
+  case 2: return tiled_by_qbw<DT, 2, ARG>(qbw, a, di, st);
+  case 4: return tiled_by_qbw<DT, 4, ARG>(qbw, a, di, st);
+  case 8: return tiled_by_qbw<DT, 8, ARG>(qbw, a, di, st);
+  }
+  return MAXSIM_ERR_UNSUPPORTED;
+}
+
+// Dense storage (bf16 / fp16 / fp32) with q_len > 64; defined in tiled_dense.hip.
+int tiled_dense_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di, hipStream_t st);
+// INT8 storage; defined in tiled_i8.hip.
+int tiled_i8_run(const TiledArgs &a, int d, const DeviceInfo &di, hipStream_t st);
+
+}  // namespace maxsim

@@ -1,0 +1,289 @@
+// Query-tiled MaxSim kernel: long queries (ColPali shape) and INT8 x INT8.
+//
+// What it computes: out[b] = sum_i max_j s(q_i, d_j) with
+//   - s = <q_i, d_j> for bf16 / fp16 / fp32 storage (TileMaxSim deep reading,
+//     section 1), or
+//   - s = fl32( fl32(dot_ij) * fl32(q_scale[i] * d_scale[j]) ) for int8 storage,
+//     dot_ij the exact int32 dot product (Flash-MaxSim abstract: INT8xINT8
+//     scoring; the per-token scales are applied as a product before the max).
+//
+// Flash-MaxSim's forward pass (Figure 1, Algorithm 2) loops over query tiles
+// inside one program per (query, document) pair; on gfx950 the query tiles run
+// concurrently instead: the 8 waves of a workgroup each hold one slice of the
+// query tokens as resident MFMA B operands (QBW blocks of 16 tokens), and one
+// copy of every document block sits in LDS for all of them.
+//  * Documents are walked by workgroup (grid stride). A block is 32 KiB of
+//    document tokens: each wave loads 4 KiB of it with 1 KiB contiguous,
+//    non-temporal loads, writes it to a double-buffered XOR-swizzled LDS tile
+//    and, after one barrier, every wave reads the block's 16-token tiles as
+//    A operands. The next block's loads are in flight while the current one is
+//    multiplied, and each document is read from HBM once for all query slices.
+//  * Rows past the document's end are clamped to its last token (a duplicate
+//    cannot change a maximum); whole tiles past the end are skipped.
+//  * Per tile and query block, the 16x16 accumulator is reduced into a running
+//    max held in one VGPR per lane (plus the argmax for the INT8 token outputs).
+//  * At the document's end each wave folds its maxima into one partial sum;
+//    the partials meet in LDS and one thread adds them in wave order. These sums
+//    over up to 1024 query tokens are taken in double and rounded once to fp32,
+//    so a score of a few hundred keeps its fp32 precision.
+#pragma once
+
+#include "device_common.hpp"
+#include "dense_kernel.hpp"
+
+namespace maxsim {
+
+constexpr int DT_I8 = 3;
+constexpr int TILED_WAVES = 8;
+constexpr int TILED_THREADS = TILED_WAVES * WAVE;
+constexpr int TILED_BLOCK_BYTES = 32 * 1024;
+
+template <> struct Elem<DT_I8> { static constexpr int bytes = 1; };
+
+// INT8: 16x16x64 i8 -> i32, K = 64 int8 = one 64-byte chunk per row.
+__device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                               __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+}
+
+struct TiledArgs {
+  const char *Q;
+  int q_len;
+  const char *D;
+  const int64_t *offsets;   // CSR, or nullptr for fixed documents of nd tokens
+  int64_t n_docs;
+  int nd;
+  const int32_t *doc_lens;  // fixed layout only, nullable
+  const float *q_scale;     // int8 only
+  const float *d_scale;     // int8 only, per document token
+  float *out;
+  float *tok_max;           // int8 only, nullable: [n_docs][q_len]
+  int32_t *tok_arg;         // int8 only, nullable: [n_docs][q_len]
+};
+
+__device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int64_t &first,
+                                             int64_t &len) {
+  if (a.offsets) {
+    const c_i64 *off = (const c_i64 *)a.offsets;
+    first = uniform(off[b]);
+    len = uniform(off[b + 1]) - first;
+  } else {
+    first = b * (int64_t)a.nd;
+    len = a.nd;
+    if (a.doc_lens) {
+      int64_t l = uniform((int64_t)((const c_i32 *)a.doc_lens)[b]);
+      len = l < 0 ? 0 : (l > a.nd ? a.nd : l);
+    }
+  }
+}
+
+// DT: storage; KSB: 64-byte chunks per token row (d = KSB * 64 / element bytes);
+// QBW: 16-query blocks per wave (queries per workgroup = 8 * 16 * QBW);
+// ARG: also produce the per-token maxima and argmax (int8 only).
+template <int DT, int KSB, int QBW, bool ARG>
+__global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a) {
+  constexpr int RB = KSB * 64;                         // bytes per token row
+  constexpr int PPR = KSB * 4;                         // 16-byte pieces per row
+  constexpr int BLK_ROWS = TILED_BLOCK_BYTES / RB;     // tokens per block
+  constexpr int BLK_TILES = BLK_ROWS / 16;
+  constexpr int LOADS = TILED_BLOCK_BYTES / (TILED_THREADS * 16);  // per lane per block
+  constexpr bool I8 = DT == DT_I8;
+  static_assert((PPR & (PPR - 1)) == 0, "swizzle needs a power-of-two row");
+  __shared__ __attribute__((aligned(16))) char blk_lds[2][TILED_BLOCK_BYTES];
+  __shared__ double part_lds[TILED_WAVES];
+  __shared__ float dscale_lds[2][I8 ? BLK_ROWS : 1];
+
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int w = uniform((int)(threadIdx.x >> 6));
+  const int q_len = a.q_len;
+  const int q_base = w * QBW * 16;
+
+  // ---- this wave's query slice, resident as B operands ----
+  u32x4_t qreg[QBW][KSB];
+  float qs[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; qb++) {
+    const int qi = q_base + qb * 16 + r16;
+    qs[qb] = 0.f;
+    if constexpr (I8) {
+      if (qi < q_len) qs[qb] = a.q_scale[qi];
+    }
+#pragma unroll
+    for (int c = 0; c < KSB; c++) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qi < q_len) v = load16(a.Q + (int64_t)qi * RB + c * 64 + g * 16);
+      qreg[qb][c] = v;
+    }
+  }
+
+  // ---- block sequence of this workgroup: (doc, block) in order ----
+  int64_t cb = blockIdx.x, cfirst = 0, clen = 0;
+  int cblk = 0;
+  if (cb < a.n_docs) tiled_extent(a, cb, cfirst, clen);
+
+  u32x4_t pre[LOADS];
+  float pre_scale = 0.f;
+  // Issue the loads of block `blk` of the document (first, len); a dummy in-bounds
+  // read of the query when there is nothing to load.
+  auto load_block = [&](bool real, int64_t first, int64_t len, int blk) {
+    const char *base = a.Q;
+    int last = 0;
+    if (real) {
+      const int64_t r0 = (int64_t)blk * BLK_ROWS;
+      const int64_t rem = len - 1 - r0;
+      last = rem < BLK_ROWS - 1 ? (int)rem : BLK_ROWS - 1;
+      base = a.D + (first + r0) * RB;
+    }
+#pragma unroll
+    for (int k = 0; k < LOADS; k++) {
+      const int u = (k * TILED_WAVES + w) * 64 + lane;  // linear 16-byte piece of the block
+      const int row = u / PPR < last ? u / PPR : last;
+      pre[k] = load16_nt(base + (int64_t)row * RB + (u % PPR) * 16);
+    }
+    if constexpr (I8) {
+      if (threadIdx.x < BLK_ROWS) {
+        const int row = (int)threadIdx.x < last ? (int)threadIdx.x : last;
+        pre_scale = real ? a.d_scale[first + (int64_t)blk * BLK_ROWS + row] : 0.f;
+      }
+    }
+  };
+  load_block(cb < a.n_docs && clen > 0, cfirst, clen, 0);
+
+  float m[QBW];
+  int arg[QBW];
+#pragma unroll
+  for (int qb = 0; qb < QBW; qb++) {
+    m[qb] = -__builtin_inff();
+    arg[qb] = -1;
+  }
+  int buf = 0;
+
+  while (cb < a.n_docs) {
+    // this block: stage the prefetched pieces in LDS
+    char *tile = blk_lds[buf];
+#pragma unroll
+    for (int k = 0; k < LOADS; k++) {
+      const int u = (k * TILED_WAVES + w) * 64 + lane, row = u / PPR, piece = u % PPR;
+      *reinterpret_cast<u32x4_t *>(tile + (row * PPR + (piece ^ stage_swizzle<PPR>(row))) * 16) =
+          pre[k];
+    }
+    if constexpr (I8) {
+      if (threadIdx.x < BLK_ROWS) dscale_lds[buf][threadIdx.x] = pre_scale;
+    }
+    const int64_t b = cb, len = clen;
+    const int blk = cblk;
+    const bool empty = len == 0;
+    const int64_t nblk = empty ? 1 : (len + BLK_ROWS - 1) / BLK_ROWS;
+    const bool doc_end = (blk == nblk - 1);
+    // advance and prefetch the next block (of this or the next document)
+    if (doc_end) {
+      cb += gridDim.x;
+      cblk = 0;
+      if (cb < a.n_docs) tiled_extent(a, cb, cfirst, clen);
+    } else {
+      cblk++;
+    }
+    load_block(cb < a.n_docs && clen > 0, cfirst, clen, cblk);
+    __syncthreads();
+
+    // multiply the block's valid tiles against this wave's query slice
+    if (!empty) {
+      const int64_t rows_left = len - (int64_t)blk * BLK_ROWS;
+      const int ntiles = rows_left >= BLK_ROWS ? BLK_TILES : (int)((rows_left + 15) >> 4);
+      for (int t = 0; t < ntiles; t++) {
+        u32x4_t aop[KSB];
+#pragma unroll
+        for (int c = 0; c < KSB; c++) {
+          const int row = t * 16 + r16;
+          aop[c] = *reinterpret_cast<const u32x4_t *>(
+              tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
+        }
+        if constexpr (I8) {
+          // scaled similarity per row, then the running max (ties keep the lowest row)
+          const int row0 = t * 16 + 4 * g;
+          float ds[4];
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int rr = row0 + r;
+            ds[r] = dscale_lds[buf][rr];
+          }
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) {
+            i32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < KSB; c++) acc = chunk_mfma_i8(aop[c], qreg[qb][c], acc);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const float sc = __fmul_rn(qs[qb], ds[r]);
+              const float v = __fmul_rn((float)acc[r], sc);
+              // rows past the end duplicate the last token: only a strictly larger
+              // value replaces the maximum, so their index is never taken
+              if (v > m[qb]) {
+                m[qb] = v;
+                if constexpr (ARG) arg[qb] = blk * BLK_ROWS + row0 + r;
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KSB; c++) acc = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc);
+            m[qb] = __builtin_fmaxf(m[qb], max4(acc));
+          }
+        }
+      }
+    }
+
+    if (doc_end) {
+      double s = 0.0;
+#pragma unroll
+      for (int qb = 0; qb < QBW; qb++) {
+        float v = m[qb];
+        int j = arg[qb];
+        // combine the four row groups: larger value wins, equal values keep the lower row
+#pragma unroll
+        for (int sh = 16; sh <= 32; sh <<= 1) {
+          const float ov = __shfl_xor(v, sh);
+          const int oj = __shfl_xor(j, sh);
+          if (ARG) {
+            if (ov > v || (ov == v && oj < j)) {
+              v = ov;
+              j = oj;
+            }
+          } else {
+            v = __builtin_fmaxf(v, ov);
+          }
+        }
+        const int qi = q_base + qb * 16 + r16;
+        if (qi < q_len) {
+          s += empty ? 0.0 : (double)v;
+          if constexpr (ARG) {
+            if (g == 0) {
+              a.tok_max[b * q_len + qi] = empty ? -__builtin_inff() : v;
+              a.tok_arg[b * q_len + qi] = empty ? -1 : j;
+            }
+          }
+        }
+        m[qb] = -__builtin_inff();
+        arg[qb] = -1;
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 8);
+      if (lane == 0) part_lds[w] = s;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int k = 0; k < TILED_WAVES; k++) tot += part_lds[k];
+        a.out[b] = empty ? -__builtin_inff() : (float)tot;
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+}  // namespace maxsim
