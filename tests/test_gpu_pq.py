@@ -1,0 +1,101 @@
+"""GPU parity of the product-quantisation path: table build and fused lookup scoring,
+against the oracle with the same codebook and codes (|delta| <= 1e-3)."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from gpu_util import PQ_TOL, compare, ms, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ms()
+
+
+def gpu_tables(Q, dtype, C):
+    import torch
+    T = ms().maxsim_pq_tables(gen.to_device(Q, dtype), torch.from_numpy(C).cuda())
+    torch.cuda.synchronize()
+    return T
+
+
+def gpu_pq(T, codes, offsets=None, nd=0):
+    import torch
+    off = None if offsets is None else torch.from_numpy(offsets).cuda()
+    out = ms().maxsim_score_pq(T, torch.from_numpy(codes).cuda(), off, nd=nd)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("dsub,M", [(8, 16), (4, 16), (2, 16), (16, 8)])
+def test_tables(dtype, dsub, M):
+    say(f"case: PQ tables {dtype} M={M} dsub={dsub}")
+    C = gen.codebook(41, M, 256, dsub)
+    Q = gen.tokens(41, gen.S_QUERY, 0, 32, M * dsub, dtype)
+    want = oracle.pq_tables(Q, dtype, C)
+    got = gpu_tables(Q, dtype, C).cpu().numpy().astype(np.float64)
+    err = np.abs(got - want).max()
+    say(f"  tables max |gpu - oracle| = {err:.2e}")
+    assert err <= 1e-6
+
+
+@pytest.mark.parametrize("q_len", [1, 7, 8, 9, 32, 64])
+@pytest.mark.parametrize("n_docs", [1, 63, 64, 65, 200])
+def test_score_fixed(q_len, n_docs):
+    say(f"case: PQ fixed q_len={q_len} n_docs={n_docs} nd=128")
+    C = gen.codebook(42)
+    Q = gen.tokens(42, gen.S_QUERY, 0, q_len, 128, "bf16")
+    codes = gen.codes(42, n_docs * 128)
+    T = gpu_tables(Q, "bf16", C)
+    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, nd=128)
+    compare(gpu_pq(T, codes, nd=128), want, tol=PQ_TOL, what=f"PQ fixed q={q_len} B={n_docs}")
+
+
+def test_score_uses_given_tables_exactly():
+    """Scores computed from the oracle's tables (rounded to fp32) match the oracle run on
+    the same fp32 tables: only the fp32 additions differ."""
+    import torch
+    say("case: PQ scorer on oracle tables")
+    C = gen.codebook(43)
+    Q = gen.tokens(43, gen.S_QUERY, 0, 32, 128, "bf16")
+    T32 = oracle.pq_tables(Q, "bf16", C).astype(np.float32)
+    codes = gen.codes(43, 300 * 40)
+    want = oracle.maxsim_pq(T32.astype(np.float64), codes, nd=40)
+    got = gpu_pq(torch.from_numpy(T32).cuda(), codes, nd=40)
+    compare(got, want, tol=1e-4, what="PQ on fixed tables")
+
+
+def test_score_csr_ragged_with_empty_docs():
+    lens = np.concatenate([[0, 1, 512, 0, 128, 129, 7],
+                           gen.lengths(44, 250)]).astype(np.int64)
+    say(f"case: PQ CSR {len(lens)} docs incl. empty")
+    off = gen.csr_offsets(lens)
+    C = gen.codebook(44)
+    Q = gen.tokens(44, gen.S_QUERY, 0, 32, 128, "bf16")
+    codes = gen.codes(44, int(off[-1]))
+    T = gpu_tables(Q, "bf16", C)
+    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, offsets=off)
+    got = gpu_pq(T, codes, offsets=off)
+    assert np.all(np.isneginf(got[lens == 0]))
+    compare(got, want, tol=PQ_TOL, what="PQ CSR")
+
+
+def test_planted_docs_rank_first_after_encoding():
+    """Planted near-duplicates stay on top after nearest-centroid PQ encoding."""
+    say("case: PQ planted top-k")
+    c = gen.csr_corpus(45, 400, 32, 128, "bf16", n_plant=5)
+    x = (c.D.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    C = gen.codebook(45)
+    codes = gen.pq_encode(x, C)
+    T = gpu_tables(c.Q, "bf16", C)
+    got = gpu_pq(T, codes, offsets=c.offsets)
+    want = oracle.maxsim_pq(oracle.pq_tables(c.Q, "bf16", C), codes, offsets=c.offsets)
+    compare(got, want, tol=PQ_TOL, what="PQ planted")
+    top = np.lexsort((np.arange(len(got)), -got))[:5]
+    assert set(top.tolist()) == set(c.planted.tolist())
