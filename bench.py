@@ -1,15 +1,16 @@
 #!/usr/bin/env python3
-"""MaxSim scoring benchmark on one MI355X: docs/s and achieved HBM bandwidth.
+"""MaxSim scoring benchmark on one MI355X: docs/s and achieved bandwidth or throughput.
 
-A step is one call of the scoring path over the whole synthetic corpus, inputs
+A step is one pass of the scoring path over the whole synthetic corpus, inputs
 already resident in HBM. The default workload is the ColBERTv2 shape the pages
 quote their headline on (TileMaxSim deep reading, section 4, Table 1): one query
 of 32 tokens against 100,000 documents of 128 tokens, d=128, bf16.
 
-Prints one JSON line. `roofline` covers the scoring kernel: algorithmic bytes per
-launch divided by its average duration, measured with HIP events recorded on the
-stream the kernel runs on. `cpu_baseline` times the float64 oracle on a bounded
-sample of the same workload on the host cores.
+Prints one JSON line. `roofline` covers the step's dominant kernel: algorithmic
+bytes (memory-bound paths), FLOPs / integer ops (matrix-core-bound paths) or
+table-lookup bytes (PQ) per launch, divided by its average duration measured with
+HIP events recorded on the stream the kernel runs on. `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -23,29 +24,51 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+# MI355X published peaks (dense): HBM3E 8 TB/s; MFMA bf16/fp16 2.5 PFLOP/s, int8 5.0 POP/s,
+# fp32 157.3 TFLOP/s. LDS: 256 CUs x 128 B/clk x 2.4 GHz (derived, see the design notes).
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3, "i8": 5000.0}
+LDS_PEAK_GBS = 256 * 128 * 2.4
 METRIC = "docs/s + % HBM peak, MaxSim B=100K Nq=32 Nd=128 d=128 bf16"
 
-# name -> workload. kind: fixed (D [B, nd, d]) or csr (lognormal lengths, median 70, 8..512)
+# layout: fixed (D [B, nd, d]) or csr (lognormal lengths, median 70, sigma 0.5, 8..512).
+# path: dense (bf16/fp16/fp32), i8 (INT8 x INT8, per-token scales), pq (tables + lookups).
+# pool: build the corpus from this many distinct seeded documents repeated to B.
+_CB = dict(layout="fixed", path="dense", q_len=32, nd=128, d=128, dtype="bf16", seed=2)
 WORKLOADS = {
-    "colbert-b100k": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=128, dtype="bf16", seed=2),
-    "colbert-b1k": dict(kind="fixed", B=1_000, q_len=32, nd=128, d=128, dtype="bf16", seed=2),
-    "colbert-b10k": dict(kind="fixed", B=10_000, q_len=32, nd=128, d=128, dtype="bf16", seed=2),
-    "colbert-b500k": dict(kind="fixed", B=500_000, q_len=32, nd=128, d=128, dtype="bf16", seed=2),
-    "colbert-nd32": dict(kind="fixed", B=100_000, q_len=32, nd=32, d=128, dtype="bf16", seed=2),
-    "colbert-nd64": dict(kind="fixed", B=100_000, q_len=32, nd=64, d=128, dtype="bf16", seed=2),
-    "colbert-nd256": dict(kind="fixed", B=100_000, q_len=32, nd=256, d=128, dtype="bf16", seed=2),
-    "colbert-nd512": dict(kind="fixed", B=100_000, q_len=32, nd=512, d=128, dtype="bf16", seed=2),
-    "colbert-fp16": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=128, dtype="fp16", seed=2),
-    "colbert-fp32": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=128, dtype="fp32", seed=2),
-    "dtile-d64": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=64, dtype="bf16", seed=3),
-    "dtile-d256": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=256, dtype="bf16", seed=3),
-    "dtile-d768": dict(kind="fixed", B=100_000, q_len=32, nd=128, d=768, dtype="bf16", seed=3),
-    "csr-bf16": dict(kind="csr", B=100_000, q_len=32, d=128, dtype="bf16", seed=5),
+    "colbert-b100k": dict(_CB, B=100_000),
+    "colbert-b1k": dict(_CB, B=1_000),
+    "colbert-b10k": dict(_CB, B=10_000),
+    "colbert-b500k": dict(_CB, B=500_000, pool=50_000),
+    "colbert-nd32": dict(_CB, B=100_000, nd=32),
+    "colbert-nd64": dict(_CB, B=100_000, nd=64),
+    "colbert-nd256": dict(_CB, B=100_000, nd=256),
+    "colbert-nd512": dict(_CB, B=100_000, nd=512, pool=50_000),
+    "colbert-fp16": dict(_CB, B=100_000, dtype="fp16"),
+    "colbert-fp32": dict(_CB, B=100_000, dtype="fp32"),
+    "dtile-d64": dict(_CB, B=100_000, d=64, seed=3),
+    "dtile-d256": dict(_CB, B=100_000, d=256, seed=3),
+    "dtile-d768": dict(_CB, B=100_000, d=768, seed=3, pool=25_000),
+    "colpali-bf16-b1k": dict(_CB, B=1_000, q_len=1024, nd=1024, seed=4),
+    "colpali-bf16-b10k": dict(_CB, B=10_000, q_len=1024, nd=1024, seed=4, pool=2_048),
+    "colpali-bf16-b50k": dict(_CB, B=50_000, q_len=1024, nd=1024, seed=4, pool=2_048),
+    "colpali-bf16-b175k": dict(_CB, B=175_000, q_len=1024, nd=1024, seed=4, pool=2_048),
+    "colpali-i8-b1k": dict(_CB, B=1_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8"),
+    "colpali-i8-b10k": dict(_CB, B=10_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8",
+                            pool=2_048),
+    "colpali-i8-b50k": dict(_CB, B=50_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8",
+                            pool=2_048),
+    "colpali-i8-b175k": dict(_CB, B=175_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8",
+                             pool=2_048),
+    "csr-bf16": dict(_CB, B=100_000, layout="csr", seed=5),
+    "csr-pq": dict(_CB, B=100_000, layout="csr", seed=5, path="pq"),
+    "fixed-pq": dict(_CB, B=100_000, seed=5, path="pq"),
 }
 DEFAULT = "colbert-b100k"
-KERNEL_SOURCES = ["device_common.hpp", "dense_kernel.hpp", "dense_variants.hpp"]
+KERNEL_SOURCES = ["device_common.hpp", "dense_kernel.hpp", "dense_variants.hpp", "tiled_kernel.hpp",
+                  "pq_kernel.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PQ_M, PQ_K, PQ_DSUB = 16, 256, 8
 
 
 def log(*a):
@@ -53,6 +76,7 @@ def log(*a):
 
 
 def kernel_hash() -> str:
+    """Hash of the kernel sources, to tell whether stored counter readings still apply."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "maxsim_scoring_fwd_amd", "csrc", f), "rb").read())
@@ -60,88 +84,199 @@ def kernel_hash() -> str:
 
 
 def esize(dtype):
-    return 4 if dtype == "fp32" else 2
+    return {"bf16": 2, "fp16": 2, "fp32": 4, "i8": 1}[dtype]
+
+
+def bound_of(w):
+    if w["path"] == "pq":
+        return "lds"
+    if w["path"] == "i8" or w["q_len"] > 64:
+        return "mfma"
+    return "hbm"
+
+
+def _fill_rows(dst, seed, row0_of, nrows_total, d, dtype, device, chunk_rows, scale_dst=None):
+    """Generate stream rows [0, nrows_total) in chunks into the device tensor dst (and scales)."""
+    import torch
+
+    import gen
+    for r0 in range(0, nrows_total, chunk_rows):
+        r1 = min(nrows_total, r0 + chunk_rows)
+        if dtype == "i8":
+            q, s = gen.tokens(seed, gen.S_DOCS, row0_of + r0, r1 - r0, d, "i8")
+            dst[r0:r1] = torch.from_numpy(q).to(device)
+            scale_dst[r0:r1] = torch.from_numpy(s).to(device)
+        else:
+            dst[r0:r1] = gen.to_device(gen.tokens(seed, gen.S_DOCS, row0_of + r0, r1 - r0, d, dtype),
+                                       dtype, device)
 
 
 def make_inputs(w, device):
-    """Generate the corpus on the host in chunks and copy it to the device."""
+    """Generate the workload on the host in chunks and copy it to the device. With a pool,
+    the first `pool` documents are generated and repeated (device copies) to fill B."""
     import numpy as np
     import torch
 
     import gen
-    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w["dtype"]]
-    d, seed = w["d"], w["seed"]
-    Q = gen.to_device(gen.tokens(seed, gen.S_QUERY, 0, w["q_len"], d, w["dtype"]), w["dtype"],
-                      device)
-    if w["kind"] == "fixed":
-        B, nd = w["B"], w["nd"]
-        D = torch.empty((B, nd, d), dtype=tdt, device=device)
-        step = max(1, (1 << 28) // (nd * d * esize(w["dtype"])))
-        for b0 in range(0, B, step):
-            b1 = min(B, b0 + step)
-            D[b0:b1] = gen.to_device(gen.tokens(seed, gen.S_DOCS, b0 * nd, (b1 - b0) * nd, d,
-                                                w["dtype"]), w["dtype"], device).view(b1 - b0,
-                                                                                     nd, d)
-        return dict(Q=Q, D=D, offsets=None, n_tokens=B * nd)
-    lens = gen.lengths(seed, w["B"])
+    d, seed, dt = w["d"], w["seed"], w["dtype"]
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32,
+           "i8": torch.int8}[dt]
+    B = w["B"]
+    inp = {}
+    if dt == "i8":
+        q, qs = gen.tokens(seed, gen.S_QUERY, 0, w["q_len"], d, "i8")
+        inp["Q"] = torch.from_numpy(q).to(device)
+        inp["q_scale"] = torch.from_numpy(qs).to(device)
+    else:
+        inp["Q"] = gen.to_device(gen.tokens(seed, gen.S_QUERY, 0, w["q_len"], d, dt), dt, device)
+    chunk_rows = max(1, (1 << 28) // (d * esize(dt)))
+
+    if w["layout"] == "fixed":
+        nd = w["nd"]
+        pool = min(B, w.get("pool") or B)
+        n_tok = B * nd
+        inp["offsets"], inp["n_tokens"] = None, n_tok
+        if w["path"] == "pq":
+            C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
+            inp["C"] = torch.from_numpy(C).to(device)
+            inp["codes"] = torch.from_numpy(gen.codes(seed, n_tok, PQ_M, PQ_K)).to(device)
+            inp["T"] = torch.empty((w["q_len"], PQ_M, PQ_K), dtype=torch.float32, device=device)
+            return inp
+        D = torch.empty((B * nd, d), dtype=tdt, device=device)
+        S = torch.empty(B * nd, dtype=torch.float32, device=device) if dt == "i8" else None
+        _fill_rows(D, seed, 0, pool * nd, d, dt, device, chunk_rows, S)
+        for b0 in range(pool, B, pool):
+            b1 = min(B, b0 + pool)
+            D[b0 * nd:b1 * nd] = D[0:(b1 - b0) * nd]
+            if S is not None:
+                S[b0 * nd:b1 * nd] = S[0:(b1 - b0) * nd]
+        inp["D"] = D.view(B, nd, d)
+        inp["d_scale"] = S
+        return inp
+
+    lens = gen.lengths(seed, B)
     off = gen.csr_offsets(lens)
     T = int(off[-1])
+    inp["offsets"] = torch.from_numpy(off).to(device)
+    inp["n_tokens"] = T
+    if w["path"] == "pq":
+        C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
+        inp["C"] = torch.from_numpy(C).to(device)
+        inp["codes"] = torch.from_numpy(gen.codes(seed, T, PQ_M, PQ_K)).to(device)
+        inp["T"] = torch.empty((w["q_len"], PQ_M, PQ_K), dtype=torch.float32, device=device)
+        return inp
     D = torch.empty((T, d), dtype=tdt, device=device)
-    step = (1 << 28) // (d * esize(w["dtype"]))
-    for t0 in range(0, T, step):
-        t1 = min(T, t0 + step)
-        D[t0:t1] = gen.to_device(gen.tokens(seed, gen.S_DOCS, t0, t1 - t0, d, w["dtype"]),
-                                 w["dtype"], device)
-    return dict(Q=Q, D=D, offsets=torch.from_numpy(off).to(device), n_tokens=T,
-                offsets_np=off)
+    S = torch.empty(T, dtype=torch.float32, device=device) if dt == "i8" else None
+    _fill_rows(D, seed, 0, T, d, dt, device, chunk_rows, S)
+    inp["D"], inp["d_scale"] = D, S
+    return inp
 
 
-def alg_bytes(w, inp) -> int:
-    """Bytes the scoring kernel must move at minimum: every document token once, the query
-    once, one fp32 score per document, and the CSR offsets."""
-    eb = esize(w["dtype"])
-    b = inp["n_tokens"] * w["d"] * eb + w["q_len"] * w["d"] * eb + w["B"] * 4
-    if inp["offsets"] is not None:
-        b += (w["B"] + 1) * 8
-    return b
+def work_per_launch(w, inp):
+    """Algorithmic work of the dominant kernel per launch: (amount, unit of the rate)."""
+    n_tok, q, d, B = inp["n_tokens"], w["q_len"], w["d"], w["B"]
+    bound = bound_of(w)
+    if bound == "hbm":
+        b = n_tok * d * esize(w["dtype"]) + q * d * esize(w["dtype"]) + B * 4
+        if inp["offsets"] is not None:
+            b += (B + 1) * 8
+        return b, "GB/s"
+    if bound == "mfma":
+        return 2 * q * n_tok * d, ("TOP/s" if w["dtype"] == "i8" else "TFLOP/s")
+    return n_tok * q * PQ_M * 4, "GB/s"  # fp32 table entries looked up
 
 
-def run_step(ms, w, inp, out):
+def hbm_bytes(w, inp):
+    """Bytes every document token costs in HBM (for context on mfma / lds-bound paths)."""
+    if w["path"] == "pq":
+        return inp["n_tokens"] * PQ_M + w["B"] * 4
+    b = inp["n_tokens"] * (w["d"] * esize(w["dtype"]) + (4 if w["dtype"] == "i8" else 0))
+    return b + w["B"] * 4
+
+
+def launches(ms, w, inp, out):
+    """The kernel launches of one step, as (name, callable); the last one is dominant."""
+    if w["path"] == "pq":
+        steps = [("pq_tables", lambda: ms.maxsim_pq_tables(inp["Q"], inp["C"], T=inp["T"]))]
+        if inp["offsets"] is None:
+            steps.append(("pq_score", lambda: ms.maxsim_score_pq(inp["T"], inp["codes"], nd=w["nd"],
+                                                                 out=out)))
+        else:
+            steps.append(("pq_score", lambda: ms.maxsim_score_pq(inp["T"], inp["codes"],
+                                                                 inp["offsets"], out=out)))
+        return steps
+    if w["path"] == "i8":
+        return [("maxsim_i8", lambda: ms.maxsim_score_i8(inp["Q"], inp["q_scale"], inp["D"],
+                                                         inp["d_scale"], inp["offsets"], out=out))]
     if inp["offsets"] is None:
-        ms.maxsim_score_fixed(inp["Q"], inp["D"], out=out)
-    else:
-        ms.maxsim_score(inp["Q"], inp["D"], inp["offsets"], out=out)
+        return [("maxsim", lambda: ms.maxsim_score_fixed(inp["Q"], inp["D"], out=out))]
+    return [("maxsim", lambda: ms.maxsim_score(inp["Q"], inp["D"], inp["offsets"], out=out))]
 
 
 def cpu_baseline(w, budget_s: float):
-    """Oracle on the host cores over the first docs of the same workload, sized to ~budget_s."""
+    """Oracle on the host cores over the first documents of the same workload, sized to take
+    about budget_s seconds."""
     import numpy as np
 
     import gen
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
-    seed, d, dt = w["seed"], w["d"], w["dtype"]
-    Qh = gen.tokens(seed, gen.S_QUERY, 0, w["q_len"], d, dt)
+    seed, d, dt, q = w["seed"], w["d"], w["dtype"], w["q_len"]
 
     def score(n):
-        if w["kind"] == "fixed":
-            Dh = gen.tokens(seed, gen.S_DOCS, 0, n * w["nd"], d, dt).reshape(n, w["nd"], d)
-            t = time.perf_counter()
-            oracle.maxsim_fixed(Qh, Dh, dt, nthreads=threads)
+        if w["layout"] == "fixed":
+            off = None
+            n_tok = n * w["nd"]
         else:
             off = gen.csr_offsets(gen.lengths(seed, w["B"])[:n])
-            Dh = gen.tokens(seed, gen.S_DOCS, 0, int(off[-1]), d, dt)
+            n_tok = int(off[-1])
+        if w["path"] == "pq":
+            Qh = gen.tokens(seed, gen.S_QUERY, 0, q, d, dt)
+            C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
+            codes = gen.codes(seed, n_tok, PQ_M, PQ_K)
             t = time.perf_counter()
+            T = oracle.pq_tables(Qh, dt, C)
+            oracle.maxsim_pq(T, codes, offsets=off, nd=w.get("nd", 0), nthreads=threads)
+            return time.perf_counter() - t
+        if dt == "i8":
+            Qh, qs = gen.tokens(seed, gen.S_QUERY, 0, q, d, "i8")
+            Dh, ds = gen.tokens(seed, gen.S_DOCS, 0, n_tok, d, "i8")
+            if off is None:
+                Dh, ds = Dh.reshape(n, w["nd"], d), ds.reshape(n, w["nd"])
+            t = time.perf_counter()
+            oracle.maxsim_i8(Qh, qs, Dh, ds, off, nthreads=threads)
+            return time.perf_counter() - t
+        Qh = gen.tokens(seed, gen.S_QUERY, 0, q, d, dt)
+        Dh = gen.tokens(seed, gen.S_DOCS, 0, n_tok, d, dt)
+        t = time.perf_counter()
+        if off is None:
+            oracle.maxsim_fixed(Qh, Dh.reshape(n, w["nd"], d), dt, nthreads=threads)
+        else:
             oracle.maxsim_csr(Qh, Dh, off, dt, nthreads=threads)
         return time.perf_counter() - t
 
-    n0 = min(w["B"], 256)
+    n0 = min(w["B"], 16 if q > 64 else 256)
     t0 = score(n0)
     n = int(min(w["B"], max(n0, n0 * budget_s / max(t0, 1e-6))))
     t = score(n) if n > n0 else t0
     return {"value": round(n / t, 1), "unit": "docs/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {w['B']} documents of the same workload "
                       f"(float64 oracle, {t:.1f} s)"}
+
+
+def copy_probe(mib: int, steps: int):
+    """Run the plain 128-bit copy kernel on a buffer of known size (counter calibration)."""
+    import torch
+
+    import maxsim_scoring_fwd_amd as ms
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        ms.calib_copy(src, dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "launches": steps}), flush=True)
 
 
 def main():
@@ -153,6 +288,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--no-calib", action="store_true", help="skip the stream-read calibration")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run the copy kernel on this many MiB, --steps times")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -161,6 +298,9 @@ def main():
               "shards across GPUs by documents with no exchange; run it with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
 
     import torch
 
@@ -175,46 +315,59 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t:.1f} s)")
     out = torch.empty(w["B"], dtype=torch.float32, device=dev)
-    nbytes = alg_bytes(w, inp)
+    steps_fns = launches(ms, w, inp, out)
+    work, rate_unit = work_per_launch(w, inp)
 
-    # Caches: the MI355X L2 + Infinity Cache hold ~288 MiB. Smaller corpora are flushed
-    # between steps and their throughput is taken from the kernel events only.
-    footprint = inp["D"].numel() * inp["D"].element_size()
+    # The MI355X L2 + Infinity Cache hold ~288 MiB: smaller corpora are flushed between
+    # steps and their throughput is taken from the kernel events alone.
+    footprint = hbm_bytes(w, inp)
     flush = footprint < (1 << 30)
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev) if flush else None
 
+    def one_step(evs=None):
+        for k, (_, fn) in enumerate(steps_fns):
+            if evs is not None:
+                evs[k].record(stream)
+            fn()
+        if evs is not None:
+            evs[-1].record(stream)
+
+    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        run_step(ms, w, inp, out)
+        one_step()
         if flush:
             scratch.zero_()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    nk = len(steps_fns)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        run_step(ms, w, inp, out)
-        ends[i].record(stream)
+        one_step(evs[i])
         if flush:
             scratch.zero_()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = sum(kern_ms) / len(kern_ms)
-    log(f"timed {args.steps} steps: wall {wall * 1e3 / args.steps:.4f} ms/step, "
-        f"kernel avg {avg_ms:.4f} ms, min {min(kern_ms):.4f} ms")
+    step_ms = [e[0].elapsed_time(e[-1]) for e in evs]
+    dom_ms = [e[-2].elapsed_time(e[-1]) for e in evs]  # the dominant (last) kernel
+    avg_step, avg_dom = sum(step_ms) / len(step_ms), sum(dom_ms) / len(dom_ms)
+    log(f"timed {args.steps} steps: wall {wall * 1e3 / args.steps:.4f} ms/step, step events avg "
+        f"{avg_step:.4f} ms, dominant kernel avg {avg_dom:.4f} ms, min {min(dom_ms):.4f} ms")
 
-    achieved = nbytes / (avg_ms * 1e-3) / 1e9
     if flush:
-        value = w["B"] / (avg_ms * 1e-3)
-        ms_per_step = avg_ms
+        value, ms_per_step = w["B"] / (avg_step * 1e-3), avg_step
     else:
-        value = w["B"] * args.steps / wall
-        ms_per_step = wall * 1e3 / args.steps
+        value, ms_per_step = w["B"] * args.steps / wall, wall * 1e3 / args.steps
+
+    bound = bound_of(w)
+    if bound == "mfma":
+        achieved = work / (avg_dom * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[w["dtype"]]
+    else:
+        achieved = work / (avg_dom * 1e-3) / 1e9
+        peak = HBM_PEAK_GBS if bound == "hbm" else LDS_PEAK_GBS
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -222,8 +375,13 @@ def main():
         if rec and rec.get("kernel_hash") == kernel_hash():
             traffic = rec.get("bytes_per_launch")
 
-    context = {"kernel_ms_avg": round(avg_ms, 5), "kernel_ms_min": round(min(kern_ms), 5),
-               "alg_bytes_per_launch": nbytes}
+    context = {"dominant_kernel": steps_fns[-1][0], "kernel_ms_avg": round(avg_dom, 5),
+               "kernel_ms_min": round(min(dom_ms), 5), "work_per_launch": work,
+               "hbm_bytes_per_step": footprint,
+               "hbm_GBps": round(footprint / (avg_step * 1e-3) / 1e9, 1),
+               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash()}
+    if w.get("pool") and w["pool"] < w["B"]:
+        context["pool"] = f"{w['pool']} distinct documents repeated to {w['B']}"
     if not args.no_calib:
         buf = torch.empty(1 << 30, dtype=torch.int32, device=dev)  # 4 GiB
         buf.fill_(1)
@@ -240,7 +398,8 @@ def main():
         cal_ms = sorted(s.elapsed_time(e) for s, e in zip(cs, ce))[5]
         stream_gbs = buf.numel() * 4 / (cal_ms * 1e-3) / 1e9
         context["stream_read_GBps"] = round(stream_gbs, 1)
-        context["frac_of_stream_read"] = round(achieved / stream_gbs, 4)
+        if bound == "hbm":
+            context["frac_of_stream_read"] = round(achieved / stream_gbs, 4)
         del buf
         log(f"stream-read ceiling {stream_gbs:.0f} GB/s")
 
@@ -250,13 +409,15 @@ def main():
         cpu = cpu_baseline(w, args.cpu_budget)
         log(f"cpu baseline {cpu}")
 
-    cfg = {"workload": args.workload, "kind": w["kind"], "n_docs": w["B"], "q_len": w["q_len"],
-           "d": w["d"], "storage": w["dtype"]}
-    if w["kind"] == "fixed":
+    cfg = {"workload": args.workload, "layout": w["layout"], "path": w["path"], "n_docs": w["B"],
+           "q_len": w["q_len"], "d": w["d"], "storage": w["dtype"]}
+    if w["layout"] == "fixed":
         cfg["nd"] = w["nd"]
     else:
         cfg["n_tokens"] = inp["n_tokens"]
         cfg["lengths"] = "lognormal median 70 sigma 0.5 clipped 8..512"
+    if w["path"] == "pq":
+        cfg["pq"] = {"M": PQ_M, "K": PQ_K, "dsub": PQ_DSUB}
     line = {
         "metric": METRIC if args.workload == DEFAULT else f"docs/s, MaxSim {args.workload}",
         "value": round(value, 1),
@@ -268,12 +429,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w["dtype"],
+        "dtype": {"i8": "int8", "fp32": "fp32"}.get(w["dtype"], w["dtype"]),
         "data": "synthetic (seeded unit-norm Gaussian token embeddings)",
         "config": cfg,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": rate_unit, "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "context": context,
     }

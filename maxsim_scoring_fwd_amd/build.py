@@ -18,6 +18,9 @@ HIP_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    # NaN inputs are outside the contract (include/maxsim.h): maxima need no NaN
+    # canonicalisation. Infinities are kept (-inf is the identity of a max).
+    "-fno-honor-nans",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-pass-failed",

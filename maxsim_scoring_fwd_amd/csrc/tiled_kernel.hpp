@@ -199,40 +199,51 @@ __global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a
           aop[c] = *reinterpret_cast<const u32x4_t *>(
               tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
         }
+        // all query blocks' accumulators are live: consecutive MFMAs are independent
         if constexpr (I8) {
+          i32x4_t acc[QBW];
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) acc[qb] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < KSB; c++)
+#pragma unroll
+            for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(aop[c], qreg[qb][c], acc[qb]);
           // scaled similarity per row, then the running max (ties keep the lowest row)
           const int row0 = t * 16 + 4 * g;
           float ds[4];
 #pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const int rr = row0 + r;
-            ds[r] = dscale_lds[buf][rr];
-          }
+          for (int r = 0; r < 4; r++) ds[r] = dscale_lds[buf][row0 + r];
 #pragma unroll
           for (int qb = 0; qb < QBW; qb++) {
-            i32x4_t acc = {0, 0, 0, 0};
+            float v[4];
 #pragma unroll
-            for (int c = 0; c < KSB; c++) acc = chunk_mfma_i8(aop[c], qreg[qb][c], acc);
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              const float sc = __fmul_rn(qs[qb], ds[r]);
-              const float v = __fmul_rn((float)acc[r], sc);
+            for (int r = 0; r < 4; r++) v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
+            if constexpr (ARG) {
               // rows past the end duplicate the last token: only a strictly larger
               // value replaces the maximum, so their index is never taken
-              if (v > m[qb]) {
-                m[qb] = v;
-                if constexpr (ARG) arg[qb] = blk * BLK_ROWS + row0 + r;
+#pragma unroll
+              for (int r = 0; r < 4; r++) {
+                if (v[r] > m[qb]) {
+                  m[qb] = v[r];
+                  arg[qb] = blk * BLK_ROWS + row0 + r;
+                }
               }
+            } else {
+              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[0]), v[1]);
+              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[2]), v[3]);
             }
           }
         } else {
+          f32x4_t acc[QBW];
 #pragma unroll
-          for (int qb = 0; qb < QBW; qb++) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          for (int qb = 0; qb < QBW; qb++) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < KSB; c++) acc = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc);
-            m[qb] = __builtin_fmaxf(m[qb], max4(acc));
-          }
+          for (int c = 0; c < KSB; c++)
+#pragma unroll
+            for (int qb = 0; qb < QBW; qb++)
+              acc[qb] = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc[qb]);
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
         }
       }
     }
