@@ -76,10 +76,13 @@ def log(*a):
 
 
 def kernel_hash() -> str:
-    """Hash of the kernel sources, to tell whether stored counter readings still apply."""
+    """Hash of the kernel sources and compile flags, to tell whether stored counter readings
+    still apply to the kernels that run."""
+    from maxsim_scoring_fwd_amd import build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "maxsim_scoring_fwd_amd", "csrc", f), "rb").read())
+    h.update(" ".join(build.HIP_FLAGS[:-2]).encode())  # flags without the include path
     return h.hexdigest()[:16]
 
 
