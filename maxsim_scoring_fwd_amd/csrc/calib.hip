@@ -11,14 +11,13 @@ using maxsim::u32x4_t;
 
 constexpr int CAL_THREADS = 256;
 
-// Each wave reads whole 16 KiB blocks: 16 loads of 1 KiB per lane group in flight,
+// Each wave reads whole blocks of LOADS KiB: LOADS loads of 1 KiB in flight per wave,
 // every load instruction covering 1 KiB of contiguous memory.
-constexpr int CAL_LOADS = 16;
-constexpr size_t CAL_BLOCK16 = 64 * CAL_LOADS;  // 16-byte pieces per block
-
-template <bool NT>
+template <bool NT, int LOADS>
 __global__ void __launch_bounds__(CAL_THREADS) calib_read_kernel(const u32x4_t *src, size_t n16,
                                                                  uint32_t *sink) {
+  constexpr int CAL_LOADS = LOADS;
+  constexpr size_t CAL_BLOCK16 = 64 * CAL_LOADS;  // 16-byte pieces per block
   const int lane = threadIdx.x & 63;
   const size_t wave = (size_t)blockIdx.x * (CAL_THREADS / 64) + (threadIdx.x >> 6);
   const size_t nwaves = (size_t)gridDim.x * (CAL_THREADS / 64);
@@ -57,7 +56,10 @@ extern "C" int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, 
   int rc = maxsim::current_device(di);
   if (rc != MAXSIM_OK) return rc;
   static const int nt = maxsim::env_knob("MAXSIM_CALIB_NT", 1);
-  auto kern = nt ? calib_read_kernel<true> : calib_read_kernel<false>;
+  static const int loads = maxsim::env_knob("MAXSIM_CALIB_LOADS", 16);
+  auto kern = nt ? calib_read_kernel<true, 16> : calib_read_kernel<false, 16>;
+  if (loads == 8) kern = nt ? calib_read_kernel<true, 8> : calib_read_kernel<false, 8>;
+  if (loads == 32) kern = nt ? calib_read_kernel<true, 32> : calib_read_kernel<false, 32>;
   const int bpc = maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
   hipLaunchKernelGGL(kern, dim3(bpc * di.cus), dim3(CAL_THREADS), 0, (hipStream_t)stream,
                      (const u32x4_t *)src, bytes / 16, sink);

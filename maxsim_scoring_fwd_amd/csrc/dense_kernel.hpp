@@ -5,10 +5,13 @@
 //   similarity tile held in matrix-core accumulators and never stored.
 //
 // Design for gfx950 (differs from the pages' Triton/SRAM design where noted):
-//  * One wave owns one document at a time and walks documents with a stride of
-//    the number of waves in the grid (persistent grid sized to fill every CU).
-//    Documents are independent units (Flash-MaxSim Figure 1: one program per
-//    (query, document) pair); there is no cross-wave communication.
+//  * One wave owns one document at a time (Flash-MaxSim Figure 1: one program
+//    per (query, document) pair); there is no cross-wave communication. The
+//    grid is persistent, sized to fill every CU. Fixed-length documents are
+//    walked with a stride of the number of waves. CSR documents of varying
+//    length are split into contiguous, token-balanced document ranges: each
+//    wave finds its range with a 64-way parallel search over the offsets, so
+//    no wave is left with a long tail of work.
 //  * All query tokens stay on chip for the whole kernel (TileMaxSim section 2
 //    item (1): BQ = Nq, single pass), so every document byte is read from HBM
 //    once. Up to 32 query tokens with d <= 256 live in VGPRs as ready-made MFMA
@@ -94,6 +97,28 @@ __device__ __forceinline__ void doc_extent(const DenseArgs &a, int64_t b, int64_
   }
 }
 
+// First index i in [0, n) with off[i] >= target, or n if none (off non-decreasing).
+// Each round probes 64 evenly spaced entries with one vector load per lane and
+// narrows the range 64-fold: about log64(n) dependent loads.
+__device__ __forceinline__ int64_t wave_lower_bound(const int64_t *off, int64_t n, int64_t target,
+                                                    int lane) {
+  int64_t lo = 0, hi = n;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int64_t step = (hi - lo + WAVE - 1) / WAVE;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool less = idx < hi && off[idx] < target;
+    const int cnt = __popcll(__ballot(less));  // probes below target form a prefix
+    if (cnt == 0) return lo;
+    const int64_t last_less = lo + (int64_t)(cnt - 1) * step;
+    const int64_t next = last_less + step;
+    lo = last_less + 1;
+    hi = next < hi ? next : hi;
+    lo = uniform(lo);
+    hi = uniform(hi);
+  }
+  return lo;
+}
+
 // Per-slot state of the load ring (wave-uniform). The flags are kept as separate
 // booleans: packed into one integer they lead the compiler to wait for every
 // load in flight before each tile, which serialises the ring.
@@ -151,9 +176,20 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
   // ---- producer: the (doc, tile, d-block) sequence of this wave ----
   // No loops and no stores here: an empty document becomes one slot flagged
   // SLOT_EMPTY whose score (-inf, a max over no tokens) the consumer writes.
-  int64_t pb = wave, pfirst = 0, plen = 0, ptile = 0;
+  int64_t pb = wave, pend = a.n_docs, pstep = nwaves;
+  if (a.offsets) {
+    // contiguous token-balanced range: the documents starting in this wave's share
+    const int64_t t0 = uniform(a.offsets[0]);
+    const int64_t ntok = uniform(a.offsets[a.n_docs]) - t0;
+    const int64_t lo = t0 + ntok * wave / nwaves, hi = t0 + ntok * (wave + 1) / nwaves;
+    pb = uniform(wave_lower_bound(a.offsets, a.n_docs + 1, lo, lane));
+    pend = wave == nwaves - 1 ? a.n_docs : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, hi, lane));
+    if (wave == 0) pb = 0;
+    pstep = 1;
+  }
+  int64_t pfirst = 0, plen = 0, ptile = 0;
   int pk = 0;
-  if (pb < a.n_docs) doc_extent(a, pb, pfirst, plen);
+  if (pb < pend) doc_extent(a, pb, pfirst, plen);
 
   u32x4_t buf[P][KSB];
   Slot slot[P];
@@ -162,7 +198,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
     sl.valid = false;
     const char *base = a.Q;  // in-bounds dummy source for empty or exhausted slots
     int last = 0;            // last valid row of the tile
-    if (pb < a.n_docs) {
+    if (pb < pend) {
       sl.valid = true;
       sl.doc = pb;
       bool advance = true;
@@ -187,10 +223,10 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         }
       }
       if (advance) {
-        pb += nwaves;
+        pb += pstep;
         ptile = 0;
         pk = 0;
-        if (pb < a.n_docs) doc_extent(a, pb, pfirst, plen);
+        if (pb < pend) doc_extent(a, pb, pfirst, plen);
       }
     }
     // The same per-lane formula serves the dummy case (base = Q, last = 0: every lane

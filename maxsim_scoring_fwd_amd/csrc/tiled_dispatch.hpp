@@ -13,14 +13,14 @@ inline int tiled_qbw(int q_len) { return (q_len + TILED_WAVES * 16 - 1) / (TILED
 // the slice of one wave needs QBW * KSB * 4 VGPRs, kept at or below 128.
 inline int tiled_max_q(int ksb) { return TILED_WAVES * 16 * (32 / ksb > 16 ? 16 : 32 / ksb); }
 
-template <int DT, int KSB, int QBW, bool ARG>
+template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES>
 int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
-  auto kern = tiled_maxsim_kernel<DT, KSB, QBW, ARG>;
-  const int bpc = blocks_per_cu((const void *)kern, TILED_THREADS, 0);
+  auto kern = tiled_maxsim_kernel<DT, KSB, QBW, ARG, NW>;
+  const int bpc = blocks_per_cu((const void *)kern, NW * WAVE, 0);
   const int64_t max_wg = (int64_t)bpc * di.cus;
   int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TILED_THREADS), 0, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * WAVE), 0, st, a);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 

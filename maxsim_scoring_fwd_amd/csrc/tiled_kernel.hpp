@@ -34,8 +34,7 @@
 namespace maxsim {
 
 constexpr int DT_I8 = 3;
-constexpr int TILED_WAVES = 8;
-constexpr int TILED_THREADS = TILED_WAVES * WAVE;
+constexpr int TILED_WAVES = 8;  // default waves per workgroup (query slices)
 constexpr int TILED_BLOCK_BYTES = 32 * 1024;
 
 template <> struct Elem<DT_I8> { static constexpr int bytes = 1; };
@@ -79,9 +78,10 @@ __device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int6
 
 // DT: storage; KSB: 64-byte chunks per token row (d = KSB * 64 / element bytes);
 // QBW: 16-query blocks per wave (queries per workgroup = 8 * 16 * QBW);
-// ARG: also produce the per-token maxima and argmax (int8 only).
-template <int DT, int KSB, int QBW, bool ARG>
-__global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a) {
+// ARG: also produce the per-token maxima and argmax (int8 only); NW: waves per workgroup.
+template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES>
+__global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
+  constexpr int TILED_THREADS = NW * WAVE;
   constexpr int RB = KSB * 64;                         // bytes per token row
   constexpr int PPR = KSB * 4;                         // 16-byte pieces per row
   constexpr int BLK_ROWS = TILED_BLOCK_BYTES / RB;     // tokens per block
@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a
   constexpr bool I8 = DT == DT_I8;
   static_assert((PPR & (PPR - 1)) == 0, "swizzle needs a power-of-two row");
   __shared__ __attribute__((aligned(16))) char blk_lds[2][TILED_BLOCK_BYTES];
-  __shared__ double part_lds[TILED_WAVES];
+  __shared__ double part_lds[NW];
   __shared__ float dscale_lds[2][I8 ? BLK_ROWS : 1];
 
   const int lane = threadIdx.x & (WAVE - 1);
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a
     }
 #pragma unroll
     for (int k = 0; k < LOADS; k++) {
-      const int u = (k * TILED_WAVES + w) * 64 + lane;  // linear 16-byte piece of the block
+      const int u = (k * NW + w) * 64 + lane;  // linear 16-byte piece of the block
       const int row = u / PPR < last ? u / PPR : last;
       pre[k] = load16_nt(base + (int64_t)row * RB + (u % PPR) * 16);
     }
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a
     char *tile = blk_lds[buf];
 #pragma unroll
     for (int k = 0; k < LOADS; k++) {
-      const int u = (k * TILED_WAVES + w) * 64 + lane, row = u / PPR, piece = u % PPR;
+      const int u = (k * NW + w) * 64 + lane, row = u / PPR, piece = u % PPR;
       *reinterpret_cast<u32x4_t *>(tile + (row * PPR + (piece ^ stage_swizzle<PPR>(row))) * 16) =
           pre[k];
     }
@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(TILED_THREADS) tiled_maxsim_kernel(TiledArgs a
       __syncthreads();
       if (threadIdx.x == 0) {
         double tot = 0.0;
-        for (int k = 0; k < TILED_WAVES; k++) tot += part_lds[k];
+        for (int k = 0; k < NW; k++) tot += part_lds[k];
         a.out[b] = empty ? -__builtin_inff() : (float)tot;
       }
     }
