@@ -9,11 +9,13 @@
 // the 160 KiB LDS, so the scorer stages one slice of 8 query tokens at a time.
 //  * A workgroup of 16 waves walks chunks of 64 documents. For each 8-query
 //    slice it copies T[slice] into LDS as TL[m][k][query] (the 8 queries of one
-//    (m, k) pair share 32 contiguous bytes), then every lane scores one
-//    (token, query) pair: lanes are 8 tokens x 8 queries, 128 token slots per
-//    workgroup walk the chunk's tokens in order.
-//  * A token's maximum contribution is folded with an LDS float-max atomic into
-//    mx[doc][query]; a max does not depend on order, so scores are deterministic.
+//    (m, k) pair share 32 contiguous bytes). Two threads score each token, four
+//    query tokens each: one 128-bit LDS read per subspace fetches four table
+//    entries, so a wave instruction serves 32 tokens.
+//  * Each thread pair scores a contiguous run of the chunk's tokens, keeping the
+//    running maxima of its four query tokens in registers; when the run crosses
+//    into another document the maxima are folded into mx[doc][query] with LDS
+//    float-max atomics. A max does not depend on order: scores are deterministic.
 //  * After each slice the chunk's per-document partial sums add the slice's
 //    maxima in query order; the chunk's scores are stored after the last slice.
 //  * An empty document keeps -inf maxima and scores -inf.
@@ -31,7 +33,7 @@ constexpr int PQ_K = 256;
 constexpr int PQ_QS = 8;        // query tokens per LDS slice
 constexpr int PQ_THREADS = 1024;
 constexpr int PQ_CHUNK = 64;    // documents per chunk
-constexpr int PQ_SLOTS = PQ_THREADS / PQ_QS;  // token slots per workgroup
+constexpr int PQ_PAIRS = PQ_THREADS / 2;  // token lanes per workgroup (two threads each)
 
 struct PqTableArgs {
   const char *Q;
@@ -80,14 +82,13 @@ __global__ void __launch_bounds__(256) pq_tables_kernel(PqTableArgs a) {
 }
 
 __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
-  __shared__ float tl[PQ_M * PQ_K * PQ_QS];     // 128 KiB: TL[m][k][query]
-  __shared__ float mx[PQ_CHUNK * PQ_QS];        // running maxima of the slice
+  __shared__ __attribute__((aligned(16))) float tl[PQ_M * PQ_K * PQ_QS];  // 128 KiB: TL[m][k][query]
+  __shared__ float mx[PQ_CHUNK * PQ_QS];        // maxima of the slice, per (document, query)
   __shared__ float part[PQ_CHUNK];              // per-document partial scores
   __shared__ int32_t coff[PQ_CHUNK + 1];        // chunk-relative token offsets
   const int tid = threadIdx.x;
-  const int lane = tid & (WAVE - 1);
-  const int qi = lane & (PQ_QS - 1);            // query of this lane within the slice
-  const int slot = (tid >> 6) * (WAVE / PQ_QS) + (lane >> 3);  // token slot
+  const int pair = tid >> 1;                    // token lane: two threads per token
+  const int h = tid & 1;                        // which 4 of the slice's 8 query tokens
   const int q_len = a.q_len;
   const int nslices = (q_len + PQ_QS - 1) / PQ_QS;
   const int64_t nchunks = (a.n_docs + PQ_CHUNK - 1) / PQ_CHUNK;
@@ -96,6 +97,7 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
     const int64_t d0 = ch * PQ_CHUNK;
     const int ndc = (int)(a.n_docs - d0 < PQ_CHUNK ? a.n_docs - d0 : PQ_CHUNK);
     int64_t tok0;
+    __syncthreads();  // the previous chunk is done with coff and part
     if (a.offsets) {
       tok0 = a.offsets[d0];
       if (tid <= ndc) coff[tid] = (int32_t)(a.offsets[d0 + tid] - tok0);
@@ -104,38 +106,69 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
       if (tid <= ndc) coff[tid] = tid * a.nd;
     }
     if (tid < PQ_CHUNK) part[tid] = 0.f;
+    __syncthreads();
+
+    // this token lane's contiguous run of the chunk's tokens and the document holding
+    // its first token (largest doc with coff[doc] <= t_begin, skipping empty ones)
+    const int ntok = coff[ndc];
+    const int span = (ntok + PQ_PAIRS - 1) / PQ_PAIRS;
+    const int t_begin = pair * span < ntok ? pair * span : ntok;
+    const int t_end = t_begin + span < ntok ? t_begin + span : ntok;
+    int doc0 = 0;
+    for (int lo = 0, hi = ndc; lo < hi;) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (coff[mid] <= t_begin) lo = mid; else hi = mid - 1;
+      doc0 = lo;
+    }
 
     for (int sl = 0; sl < nslices; sl++) {
       const int q0 = sl * PQ_QS;
       __syncthreads();  // the previous slice is done with tl and mx
-      // T[q0 .. q0+7][m][k] -> TL[m][k][query]; queries past q_len read as 0
-      for (int idx = tid; idx < PQ_QS * PQ_M * (PQ_K / 4); idx += PQ_THREADS) {
-        const int qs = idx / (PQ_M * (PQ_K / 4));
-        const int rem = idx % (PQ_M * (PQ_K / 4));
-        const int m = rem / (PQ_K / 4), k4 = rem % (PQ_K / 4);
-        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (q0 + qs < q_len)
-          v = *reinterpret_cast<const f32x4_t *>(a.T + ((int64_t)(q0 + qs) * PQ_M + m) * PQ_K +
-                                                 k4 * 4);
+      // TL[m][k][0..7] = T[q0 + 0..7][m][k]: one (m, k) row of 32 bytes per thread and
+      // pass; neighbouring threads write neighbouring rows (no bank conflicts)
+      for (int mk = tid; mk < PQ_M * PQ_K; mk += PQ_THREADS) {
+        f32x4_t lo4, hi4;
 #pragma unroll
-        for (int e = 0; e < 4; e++) tl[((m * PQ_K) + k4 * 4 + e) * PQ_QS + qs] = v[e];
+        for (int e = 0; e < 4; e++) {
+          lo4[e] = q0 + e < q_len ? a.T[(int64_t)(q0 + e) * PQ_M * PQ_K + mk] : 0.f;
+          hi4[e] = q0 + 4 + e < q_len ? a.T[(int64_t)(q0 + 4 + e) * PQ_M * PQ_K + mk] : 0.f;
+        }
+        *reinterpret_cast<f32x4_t *>(&tl[mk * PQ_QS]) = lo4;
+        *reinterpret_cast<f32x4_t *>(&tl[mk * PQ_QS + 4]) = hi4;
       }
       for (int idx = tid; idx < PQ_CHUNK * PQ_QS; idx += PQ_THREADS) mx[idx] = -__builtin_inff();
       __syncthreads();
 
-      const int ntok = coff[ndc];
-      int doc = 0;  // chunk-relative document of this lane's current token (moves forward)
-      for (int t = slot; t < ntok; t += PQ_SLOTS) {
-        const u32x4_t cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t) * PQ_M);
-        float s = 0.f;
+      if (t_begin < t_end) {
+        int doc = doc0;
+        f32x4_t run = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        u32x4_t cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t_begin) * PQ_M);
+        for (int t = t_begin; t < t_end; t++) {
+          const u32x4_t cur = cw;
+          if (t + 1 < t_end)  // next token's codes in flight while this one is scored
+            cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t + 1) * PQ_M);
+          if (t >= coff[doc + 1]) {
+            // this token starts a later document: fold the run into the finished one
 #pragma unroll
-        for (int m = 0; m < PQ_M; m++) {
-          const uint32_t k = (cw[m >> 2] >> ((m & 3) * 8)) & 0xffu;
-          s += tl[(m * PQ_K + (int)k) * PQ_QS + qi];
+            for (int e = 0; e < 4; e++)
+              __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+            do doc++; while (coff[doc + 1] <= t);
+            run = f32x4_t{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+          }
+          f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < PQ_M; m++) {
+            const uint32_t k = (cur[m >> 2] >> ((m & 3) * 8)) & 0xffu;
+            s += *reinterpret_cast<const f32x4_t *>(&tl[(m * PQ_K + (int)k) * PQ_QS + 4 * h]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; e++) run[e] = __builtin_fmaxf(run[e], s[e]);
         }
-        while (coff[doc + 1] <= t) doc++;
-        __hip_atomic_fetch_max(&mx[doc * PQ_QS + qi], s, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       __syncthreads();
       if (tid < ndc) {
