@@ -27,6 +27,16 @@ extern "C" {
 int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/*
+ * Matrix-core throughput: independent MFMA chains with no memory traffic, for the
+ * achievable MFMA rate of the device. kind 0: 16x16x32 bf16, 1: 32x32x16 bf16,
+ * 2: 16x16x64 int8, 3: 32x32x32 int8. waves_per_simd in [1, 8], iters >= 1.
+ * *ops receives the FLOP (or integer op) count of the launch (host pointer);
+ * sink is a device buffer of >= 65536 floats that the kernel does not write in practice.
+ */
+int maxsim_calib_mfma(int kind, int iters, int waves_per_simd, float *sink, double *ops,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

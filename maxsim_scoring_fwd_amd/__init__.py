@@ -180,8 +180,10 @@ def _calib_lib():
         vp = ctypes.c_void_p
         L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         L.maxsim_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.maxsim_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.maxsim_calib_read.restype = ctypes.c_int
         L.maxsim_calib_copy.restype = ctypes.c_int
+        L.maxsim_calib_mfma.restype = ctypes.c_int
         L._calib_bound = True
     return L
 
@@ -197,3 +199,13 @@ def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     _check(_calib_lib().maxsim_calib_copy(_dev(src, "src"), _dev(dst, "dst"),
                                           src.numel() * src.element_size(), _stream(stream)),
            "maxsim_calib_copy")
+
+
+def calib_mfma(kind: int, iters: int, waves_per_simd: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch independent MFMA chains (kind 0: 16x16x32 bf16, 1: 32x32x16 bf16, 2: 16x16x64
+    int8, 3: 32x32x32 int8); returns the FLOP / integer-op count of the launch."""
+    ops = ctypes.c_double(0.0)
+    _check(_calib_lib().maxsim_calib_mfma(kind, iters, waves_per_simd, _dev(sink, "sink"),
+                                          ctypes.addressof(ops), _stream(stream)),
+           "maxsim_calib_mfma")
+    return ops.value

@@ -23,6 +23,9 @@ HIP_FLAGS = [
     "-fno-honor-nans",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results stay in ordinary VGPRs: without it the accumulators live in
+    # AGPRs and are copied to VGPRs for every max reduction
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-pass-failed",
     "-I", os.path.join(ROOT, "include"),
 ]

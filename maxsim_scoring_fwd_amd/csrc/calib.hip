@@ -1,6 +1,8 @@
 // Streaming read and copy kernels used to calibrate bandwidth measurements.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "../../include/maxsim_calib.h"
 #include "device_common.hpp"
 #include "host_common.hpp"
@@ -75,5 +77,90 @@ extern "C" int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void 
   const int bpc = maxsim::blocks_per_cu((const void *)calib_copy_kernel, CAL_THREADS, 0);
   hipLaunchKernelGGL(calib_copy_kernel, dim3(bpc * di.cus), dim3(CAL_THREADS), 0,
                      (hipStream_t)stream, (const u32x4_t *)src, (u32x4_t *)dst, bytes / 16);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+// ---- matrix-core throughput: independent MFMA chains, no memory traffic ----
+
+namespace {
+
+using maxsim::f32x4_t;
+using maxsim::i32x4_t;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int32_t i32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int MF_CHAINS = 8;
+
+template <int KIND>
+__global__ void __launch_bounds__(256) calib_mfma_kernel(int iters, float *sink) {
+  const int lane = threadIdx.x & 63;
+  u32x4_t a = {(uint32_t)lane, 1u, 2u, 3u}, b = {3u, (uint32_t)lane, 1u, 0x3f80u};
+  if constexpr (KIND == 0 || KIND == 2) {
+    // 16x16 output tiles
+    typedef typename std::conditional<KIND == 0, f32x4_t, i32x4_t>::type acc_t;
+    acc_t acc[MF_CHAINS] = {};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int c = 0; c < MF_CHAINS; c++) {
+        if constexpr (KIND == 0)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), acc[c], 0, 0, 0);
+        else
+          acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                         __builtin_bit_cast(i32x4_t, b), acc[c], 0, 0, 0);
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < MF_CHAINS; c++) s += (float)acc[c][0] + (float)acc[c][3];
+    if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the chains alive
+  } else {
+    // 32x32 output tiles
+    typedef typename std::conditional<KIND == 1, f32x16_t, i32x16_t>::type acc_t;
+    acc_t acc[MF_CHAINS / 2] = {};
+    for (int it = 0; it < iters; it++) {
+#pragma unroll
+      for (int c = 0; c < MF_CHAINS / 2; c++) {
+        if constexpr (KIND == 1)
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), acc[c], 0, 0, 0);
+        else
+          acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
+                                                         __builtin_bit_cast(i32x4_t, b), acc[c], 0, 0, 0);
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < MF_CHAINS / 2; c++) s += (float)acc[c][0] + (float)acc[c][15];
+    if (s == 1234.5f) sink[blockIdx.x] = s;
+  }
+}
+
+}  // namespace
+
+// kind 0: 16x16x32 bf16, 1: 32x32x16 bf16, 2: 16x16x64 i8, 3: 32x32x32 i8. Launches
+// waves_per_simd x 4 x CUs waves of `iters` x 8 (16x16) or 4 (32x32) MFMAs each; returns
+// the total FLOP / integer ops in *ops. sink: >= 65536 floats, never written in practice.
+extern "C" int maxsim_calib_mfma(int kind, int iters, int waves_per_simd, float *sink,
+                                 double *ops, void *stream) {
+  if (!sink || !ops) return MAXSIM_ERR_NULL;
+  if (kind < 0 || kind > 3 || iters < 1 || waves_per_simd < 1 || waves_per_simd > 8)
+    return MAXSIM_ERR_SHAPE;
+  maxsim::DeviceInfo di;
+  int rc = maxsim::current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  const int grid = di.cus * waves_per_simd;  // 4 waves per workgroup = one per SIMD
+  const double per = kind == 0 ? 16.0 * 16 * 32 * 2 : kind == 1 ? 32.0 * 32 * 16 * 2
+                   : kind == 2 ? 16.0 * 16 * 64 * 2 : 32.0 * 32 * 32 * 2;
+  const double per_iter = kind == 0 || kind == 2 ? 8 * per : 4 * per;
+  *ops = per_iter * iters * grid * 4.0;
+  hipStream_t st = (hipStream_t)stream;
+  switch (kind) {
+  case 0: hipLaunchKernelGGL(calib_mfma_kernel<0>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  case 1: hipLaunchKernelGGL(calib_mfma_kernel<1>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  case 2: hipLaunchKernelGGL(calib_mfma_kernel<2>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  default: hipLaunchKernelGGL(calib_mfma_kernel<3>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  }
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }

@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   static_assert((PPR & (PPR - 1)) == 0, "swizzle needs a power-of-two row");
   __shared__ __attribute__((aligned(16))) char blk_lds[2][TILED_BLOCK_BYTES];
   __shared__ double part_lds[NW];
-  __shared__ float dscale_lds[2][I8 ? BLK_ROWS : 1];
+  __shared__ __attribute__((aligned(16))) float dscale_lds[2][I8 ? BLK_ROWS : 4];
 
   const int lane = threadIdx.x & (WAVE - 1);
   const int r16 = lane & 15, g = lane >> 4;
@@ -158,6 +158,10 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     arg[qb] = -1;
   }
   int buf = 0;
+  // INT8 reads the next tile's A operands while the current tile is multiplied and
+  // scaled, where the registers allow it (the query slice takes QBW * KSB * 4 VGPRs)
+  constexpr bool PREFETCH = I8 && QBW * KSB <= 16;
+  u32x4_t nxt[PREFETCH ? KSB : 1];
 
   while (cb < a.n_docs) {
     // this block: stage the prefetched pieces in LDS
@@ -191,13 +195,28 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     if (!empty) {
       const int64_t rows_left = len - (int64_t)blk * BLK_ROWS;
       const int ntiles = rows_left >= BLK_ROWS ? BLK_TILES : (int)((rows_left + 15) >> 4);
+      // A operand of chunk c of tile t: row t * 16 + r16, pieces 4c .. 4c + 3
+      auto read_a = [&](int t, int c) -> u32x4_t {
+        const int row = t * 16 + r16;
+        return *reinterpret_cast<const u32x4_t *>(
+            tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
+      };
       for (int t = 0; t < ntiles; t++) {
         u32x4_t aop[KSB];
+        if constexpr (PREFETCH) {
+          if (t == 0) {
 #pragma unroll
-        for (int c = 0; c < KSB; c++) {
-          const int row = t * 16 + r16;
-          aop[c] = *reinterpret_cast<const u32x4_t *>(
-              tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
+            for (int c = 0; c < KSB; c++) nxt[c] = read_a(0, c);
+          }
+#pragma unroll
+          for (int c = 0; c < KSB; c++) aop[c] = nxt[c];
+          if (t + 1 < ntiles) {
+#pragma unroll
+            for (int c = 0; c < KSB; c++) nxt[c] = read_a(t + 1, c);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
         }
         // all query blocks' accumulators are live: consecutive MFMAs are independent
         if constexpr (I8) {
@@ -210,9 +229,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
             for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(aop[c], qreg[qb][c], acc[qb]);
           // scaled similarity per row, then the running max (ties keep the lowest row)
           const int row0 = t * 16 + 4 * g;
-          float ds[4];
-#pragma unroll
-          for (int r = 0; r < 4; r++) ds[r] = dscale_lds[buf][row0 + r];
+          const f32x4_t ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
 #pragma unroll
           for (int qb = 0; qb < QBW; qb++) {
             float v[4];

@@ -11,6 +11,7 @@ import maxsim_scoring_fwd_amd as ms
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "maxsim.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "maxsim_calib.h")
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by these calls
@@ -24,8 +25,8 @@ def L():
     return ms.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(maxsim_\w+)\s*\(", text, re.M)))
 
@@ -43,6 +44,24 @@ def test_every_declared_symbol_is_exported(L):
     out = os.popen(f"nm -D --defined-only {ms.LIB_PATH}").read()
     exported = set(re.findall(r" T (maxsim_\w+)", out))
     assert set(declared_functions()) <= exported
+
+
+def test_calibration_symbols_are_exported(L):
+    names = declared_functions(CALIB_HEADER)
+    assert {"maxsim_calib_read", "maxsim_calib_copy", "maxsim_calib_mfma"} <= set(names)
+    out = os.popen(f"nm -D --defined-only {ms.LIB_PATH}").read()
+    assert set(names) <= set(re.findall(r" T (maxsim_\w+)", out))
+
+
+def test_calibration_argument_checks(L):
+    ops = ctypes.c_double(0.0)
+    f = L.maxsim_calib_mfma
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert f(0, 10, 1, None, ctypes.addressof(ops), None) == NULL
+    assert f(4, 10, 1, P, ctypes.addressof(ops), None) == SHAPE
+    assert f(0, 0, 1, P, ctypes.addressof(ops), None) == SHAPE
+    assert f(0, 10, 9, P, ctypes.addressof(ops), None) == SHAPE
 
 
 def test_no_torch_in_signatures():
