@@ -65,8 +65,9 @@ WORKLOADS = {
     "fixed-pq": dict(_CB, B=100_000, seed=5, path="pq"),
 }
 DEFAULT = "colbert-b100k"
-KERNEL_SOURCES = ["device_common.hpp", "dense_kernel.hpp", "dense_variants.hpp", "tiled_kernel.hpp",
-                  "pq_kernel.hpp"]
+# sources the dense bf16 kernel is built from (the kernel whose HBM traffic is stored)
+KERNEL_SOURCES = ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "dense_variants.hpp",
+                  "dense_dispatch.hpp", "dense_bf16.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PQ_M, PQ_K, PQ_DSUB = 16, 256, 8
 
