@@ -5,7 +5,10 @@ package. The GPU library never calls it, and it shares no code with the GPU path
 
 Definition followed (TileMaxSim deep reading, section 1; Flash-MaxSim abstract):
 score_b = sum over query tokens i of max over document tokens j of <q_i, d_j>, on
-the stored values, accumulated in float64. The C source states every reading
+the stored values, accumulated in float64. The backward pass (Flash-MaxSim
+abstract: training backward through the forward argmax) is the gradient of
+sum_b g_b * score_b: dQ[i] = sum_b g_b d_{b,j*(b,i)}, dD[b,j] = g_b * sum of the q_i
+whose argmax is j. The C source states every reading
 taken where the pages are silent (padding, empty documents, INT8 scale formula,
 PQ table layout).
 
@@ -50,8 +53,10 @@ def _bind(lib):
     lib.oracle_maxsim_i8.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, i32]
     lib.oracle_pq_tables.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp]
     lib.oracle_maxsim_pq.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, i32]
+    lib.oracle_maxsim_argmax.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, i32]
+    lib.oracle_maxsim_backward.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
     for f in ("oracle_maxsim_csr", "oracle_maxsim_fixed", "oracle_maxsim_i8", "oracle_pq_tables",
-              "oracle_maxsim_pq"):
+              "oracle_maxsim_pq", "oracle_maxsim_argmax", "oracle_maxsim_backward"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -120,6 +125,44 @@ class Oracle:
                                            _threads(nthreads)), "maxsim_i8")
         return out, tm, ta
 
+    @staticmethod
+    def _layout(D, offsets):
+        """(n_docs, nd, offsets) for fixed documents D [n_docs, nd, d] or CSR tokens D [n, d]."""
+        if offsets is None:
+            return D.shape[0], D.shape[1], None
+        off = _c(offsets, np.int64)
+        return len(off) - 1, 0, off
+
+    def maxsim_argmax(self, Q, D, dtype: str, offsets=None, nthreads=None):
+        """Scores with per-token maxima and argmax (lowest index among equal maxima).
+        Fixed layout when offsets is None (D [n_docs, nd, d]), else CSR (D [n_tokens, d]).
+        Returns (scores f64 [n_docs], tok_max f64 [n_docs, q_len], tok_arg i32 [n_docs, q_len])."""
+        Q, D = _c(Q), _c(D)
+        n_docs, nd, off = self._layout(D, offsets)
+        q_len, d = Q.shape
+        out = np.empty(n_docs, dtype=np.float64)
+        tm = np.empty((n_docs, q_len), dtype=np.float64)
+        ta = np.empty((n_docs, q_len), dtype=np.int32)
+        self._rc(self.lib.oracle_maxsim_argmax(_ptr(Q), q_len, _ptr(D), _ptr(off), n_docs, nd, d,
+                                               DTYPES[dtype], _ptr(out), _ptr(tm), _ptr(ta),
+                                               _threads(nthreads)), "maxsim_argmax")
+        return out, tm, ta
+
+    def maxsim_backward(self, Q, D, dtype: str, tok_arg, grad, offsets=None):
+        """Gradients of sum_b grad[b] * score_b for the argmax tok_arg [n_docs, q_len].
+        Returns (dQ f64 [q_len, d], dD f64 shaped like D)."""
+        Q, D = _c(Q), _c(D)
+        n_docs, nd, off = self._layout(D, offsets)
+        q_len, d = Q.shape
+        ta = _c(tok_arg, np.int32).reshape(n_docs, q_len)
+        g = _c(grad, np.float32).reshape(n_docs)
+        dQ = np.empty((q_len, d), dtype=np.float64)
+        dD = np.empty(D.shape, dtype=np.float64)
+        self._rc(self.lib.oracle_maxsim_backward(_ptr(Q), q_len, _ptr(D), _ptr(off), n_docs, nd, d,
+                                                 DTYPES[dtype], _ptr(ta), _ptr(g), _ptr(dQ),
+                                                 _ptr(dD)), "maxsim_backward")
+        return dQ, dD
+
     def pq_tables(self, Q, dtype: str, C) -> np.ndarray:
         """T[i][m][k] (float64) for query Q [q_len, M*dsub] and codebook C [M, K, dsub]."""
         Q, C = _c(Q), _c(C, np.float32)
@@ -167,6 +210,14 @@ def maxsim_i8(*a, **k):
 
 def pq_tables(*a, **k):
     return get().pq_tables(*a, **k)
+
+
+def maxsim_argmax(*a, **k):
+    return get().maxsim_argmax(*a, **k)
+
+
+def maxsim_backward(*a, **k):
+    return get().maxsim_backward(*a, **k)
 
 
 def maxsim_pq(*a, **k):

@@ -29,6 +29,15 @@
  *    is the sum over subspaces of table entries picked by its codes,
  *    s_ij = sum_m T[i][m][c_jm], then max over j and sum over i as above.
  *    Sub-vector m covers dimensions [m*dsub, (m+1)*dsub).
+ *  - per-token maxima and argmax (Flash-MaxSim abstract and the Flash-MaxSim
+ *    page: the backward pass reuses the argmax locations of the forward): the
+ *    argmax of query token i in document b is the lowest j reaching the maximum;
+ *  - gradients (Flash-MaxSim abstract: training backward pass): with upstream
+ *    gradient g_b of score_b and j*(b,i) the argmax, the score is linear in Q and
+ *    D away from ties, so
+ *        dQ[i]           = sum_b g_b * d_{b, j*(b,i)}
+ *        dD[b, j]        = g_b * sum_{i : j*(b,i) = j} q_i   (zero if no i chose j)
+ *    Documents without tokens (argmax -1) contribute nothing.
  *
  * Documents are independent, so they are split across threads; each
  * document's arithmetic is the same whatever thread runs it.
@@ -116,6 +125,8 @@ typedef struct {
   int nd;                  /* fixed layout: tokens per doc slot */
   const int32_t *doc_lens; /* fixed layout: valid tokens per doc (NULL = nd) */
   double *out;
+  double *tok_max;         /* [n_docs][q_len] per-token maxima, nullable */
+  int32_t *tok_arg;        /* [n_docs][q_len] lowest index reaching the maximum, nullable */
 } dense_ctx;
 
 static void dense_doc(void *vctx, int64_t b) {
@@ -137,12 +148,18 @@ static void dense_doc(void *vctx, int64_t b) {
   double score = 0.0;
   for (int i = 0; i < c->q_len; i++) {
     double m = -INFINITY;
+    int32_t arg = -1;
     for (int64_t j = 0; j < len; j++) {
       double s = 0.0;
       for (int k = 0; k < c->d; k++)
         s += c->q[(int64_t)i * c->d + k] * decode(c->D, c->dtype, (first + j) * c->d + k);
-      if (s > m) m = s;
+      if (s > m) { /* strict: the first maximum is kept */
+        m = s;
+        arg = (int32_t)j;
+      }
     }
+    if (c->tok_max) c->tok_max[b * c->q_len + i] = m;
+    if (c->tok_arg) c->tok_arg[b * c->q_len + i] = arg;
     score += m;
   }
   c->out[b] = score;
@@ -159,7 +176,8 @@ int oracle_maxsim_csr(const void *Q, int q_len, const void *D, const int64_t *of
                       int64_t n_docs, int d, int dtype, double *out, int nthreads) {
   if (!Q || !D || !offsets || !out || q_len < 0 || d <= 0 || n_docs < 0) return -1;
   if (dtype < OR_BF16 || dtype > OR_FP32) return -1;
-  dense_ctx c = {decode_query(Q, q_len, d, dtype), q_len, d, dtype, D, offsets, 0, NULL, out};
+  dense_ctx c = {decode_query(Q, q_len, d, dtype), q_len, d, dtype, D, offsets, 0, NULL, out,
+                 NULL, NULL};
   for_each_doc(n_docs, nthreads, dense_doc, &c);
   free((void *)c.q);
   return 0;
@@ -170,9 +188,55 @@ int oracle_maxsim_fixed(const void *Q, int q_len, const void *D, int64_t n_docs,
                         const int32_t *doc_lens, int d, int dtype, double *out, int nthreads) {
   if (!Q || !D || !out || q_len < 0 || d <= 0 || n_docs < 0 || nd < 0) return -1;
   if (dtype < OR_BF16 || dtype > OR_FP32) return -1;
-  dense_ctx c = {decode_query(Q, q_len, d, dtype), q_len, d, dtype, D, NULL, nd, doc_lens, out};
+  dense_ctx c = {decode_query(Q, q_len, d, dtype), q_len, d, dtype, D, NULL, nd, doc_lens, out,
+                 NULL, NULL};
   for_each_doc(n_docs, nthreads, dense_doc, &c);
   free((void *)c.q);
+  return 0;
+}
+
+/* Scores with per-token maxima and argmax. offsets nullable: fixed layout D[n_docs][nd][d]. */
+int oracle_maxsim_argmax(const void *Q, int q_len, const void *D, const int64_t *offsets,
+                         int64_t n_docs, int nd, int d, int dtype, double *out, double *tok_max,
+                         int32_t *tok_arg, int nthreads) {
+  if (!Q || !D || !out || !tok_max || !tok_arg || q_len < 0 || d <= 0 || n_docs < 0) return -1;
+  if (!offsets && nd < 0) return -1;
+  if (dtype < OR_BF16 || dtype > OR_FP32) return -1;
+  dense_ctx c = {decode_query(Q, q_len, d, dtype), q_len, d, dtype, D, offsets, nd, NULL, out,
+                 tok_max, tok_arg};
+  for_each_doc(n_docs, nthreads, dense_doc, &c);
+  free((void *)c.q);
+  return 0;
+}
+
+/* Gradients of sum_b grad[b] * score_b given the argmax tok_arg[n_docs][q_len]:
+ * dQ[q_len][d] and dD[n_tokens][d] (n_tokens = offsets[n_docs], or n_docs * nd), in double.
+ * An argmax outside [0, len_b) (the -1 of an empty document) contributes nothing. */
+int oracle_maxsim_backward(const void *Q, int q_len, const void *D, const int64_t *offsets,
+                           int64_t n_docs, int nd, int d, int dtype, const int32_t *tok_arg,
+                           const float *grad, double *dQ, double *dD) {
+  if (!Q || !D || !tok_arg || !grad || !dQ || !dD || q_len < 0 || d <= 0 || n_docs < 0)
+    return -1;
+  if (!offsets && nd < 0) return -1;
+  if (dtype < OR_BF16 || dtype > OR_FP32) return -1;
+  double *q = decode_query(Q, q_len, d, dtype);
+  const int64_t n_tokens = offsets ? offsets[n_docs] : n_docs * (int64_t)nd;
+  memset(dQ, 0, sizeof(double) * (size_t)q_len * (size_t)d);
+  memset(dD, 0, sizeof(double) * (size_t)n_tokens * (size_t)d);
+  for (int64_t b = 0; b < n_docs; b++) {
+    const int64_t first = offsets ? offsets[b] : b * (int64_t)nd;
+    const int64_t len = offsets ? offsets[b + 1] - offsets[b] : nd;
+    const double g = (double)grad[b];
+    for (int i = 0; i < q_len; i++) {
+      const int64_t j = tok_arg[b * q_len + i];
+      if (j < 0 || j >= len) continue;
+      for (int k = 0; k < d; k++) {
+        dQ[(int64_t)i * d + k] += g * decode(D, dtype, (first + j) * d + k);
+        dD[(first + j) * d + k] += g * q[(int64_t)i * d + k];
+      }
+    }
+  }
+  free(q);
   return 0;
 }
 

@@ -14,7 +14,10 @@ Kinds of pin used:
     indices), doc == query with exactly unit-norm dyadic tokens (score = q_len);
   - invariants: permutation of document tokens, padding and neighbour independence,
     scaling by powers of two;
-  - the planted near-duplicates of the 1000-document workload are the top-10.
+  - the planted near-duplicates of the 1000-document workload are the top-10;
+  - gradients: Euler's identity for homogeneous functions (<dQ, Q> = <dD, D> = the
+    weighted score), exact central differences on dyadic inputs, and the one-token
+    closed form; argmax against the materialised tensor with exact ties.
 """
 from __future__ import annotations
 
@@ -347,10 +350,139 @@ def pin_planted_top10(orc):
     assert s[c.planted].min() > 20.0 and others.max() < 12.0, (s[c.planted].min(), others.max())
 
 
+# ---------------------------------------------------------------- argmax and gradients
+
+def brute_argmax(qd: np.ndarray, docs: list[np.ndarray]):
+    """Per-token maxima and argmax from the materialised S (numpy's argmax returns the
+    first maximum, i.e. the lowest document index)."""
+    q_len = qd.shape[0]
+    tm = np.full((len(docs), q_len), -np.inf)
+    ta = np.full((len(docs), q_len), -1, dtype=np.int64)
+    for b, Db in enumerate(docs):
+        if Db.shape[0]:
+            S = np.einsum("ik,jk->ij", qd, Db)
+            tm[b], ta[b] = S.max(axis=1), S.argmax(axis=1)
+    return tm, ta
+
+
+def pin_argmax_brute(orc):
+    """Per-token maxima and argmax against the materialised similarity tensor, with exact
+    ties (duplicated document tokens: the lower index wins) and empty CSR documents."""
+    rng = np.random.default_rng(21)
+    for dtype in ("bf16", "fp16", "fp32"):
+        q_len, nd, d, B = 7, 9, 64, 12
+        Q = store(_unit_rows(rng, q_len, d), dtype)
+        D = store(_unit_rows(rng, B * nd, d), dtype).reshape(B, nd, d)
+        D[3, 6] = D[3, 2]          # a tie: token 2 must win over its copy at 6
+        D[5, 1:] = D[5, 0]         # all tokens equal: every argmax is 0
+        qd, Dd = dec(Q, dtype), dec(D, dtype)
+        s, tm, ta = orc.maxsim_argmax(Q, D, dtype)
+        wtm, wta = brute_argmax(qd, list(Dd))
+        assert np.array_equal(ta, wta), (dtype, "fixed argmax")
+        assert np.allclose(tm, wtm, rtol=0, atol=1e-12)
+        assert np.allclose(s, wtm.sum(axis=1), rtol=0, atol=1e-12)
+        assert np.all(ta[5] == 0)
+        lens = np.array([0, 1, 5, 0, 17, 3, 9, 2])
+        off = gen.csr_offsets(lens)
+        Dc = store(_unit_rows(rng, int(off[-1]), d), dtype)
+        Dc[off[4] + 11] = Dc[off[4] + 4]
+        docs = [dec(Dc, dtype)[off[b]:off[b + 1]] for b in range(len(lens))]
+        s, tm, ta = orc.maxsim_argmax(Q, Dc, dtype, offsets=off)
+        wtm, wta = brute_argmax(qd, docs)
+        assert np.array_equal(ta, wta), (dtype, "csr argmax")
+        assert np.all(ta[lens == 0] == -1) and np.all(np.isneginf(tm[lens == 0]))
+        fin = lens > 0
+        assert np.allclose(tm[fin], wtm[fin], rtol=0, atol=1e-12)
+        assert np.all(np.isneginf(s[~fin]))
+
+
+def _grad_case(rng, dtype, offsets_mode):
+    q_len, d = 6, 64
+    Q = store(_unit_rows(rng, q_len, d), dtype)
+    if offsets_mode:
+        lens = np.array([3, 0, 11, 1, 7, 16, 5])
+        off = gen.csr_offsets(lens)
+        D = store(_unit_rows(rng, int(off[-1]), d), dtype)
+        n_docs = len(lens)
+    else:
+        off, n_docs = None, 9
+        D = store(_unit_rows(rng, n_docs * 8, d), dtype).reshape(n_docs, 8, d)
+    g = rng.standard_normal(n_docs).astype(np.float32)
+    return Q, D, off, g
+
+
+def pin_backward_euler(orc):
+    """The score is positively homogeneous of degree one in Q and, separately, in D, so
+    by Euler's theorem <dQ, Q> = <dD, D> = sum_b g_b score_b (empty documents excluded).
+    A wrong row, a dropped factor or a wrong sign in either gradient breaks it."""
+    rng = np.random.default_rng(22)
+    for dtype in ("bf16", "fp16", "fp32"):
+        for csr in (False, True):
+            Q, D, off, g = _grad_case(rng, dtype, csr)
+            s, _, ta = orc.maxsim_argmax(Q, D, dtype, offsets=off)
+            dQ, dD = orc.maxsim_backward(Q, D, dtype, ta, g, offsets=off)
+            fin = np.isfinite(s)
+            want = float(np.sum(g[fin].astype(np.float64) * s[fin]))
+            eq = float(np.sum(dQ * dec(Q, dtype)))
+            ed = float(np.sum(dD * dec(D, dtype)))
+            assert abs(eq - want) <= 1e-9 * (1 + abs(want)), (dtype, csr, eq, want)
+            assert abs(ed - want) <= 1e-9 * (1 + abs(want)), (dtype, csr, ed, want)
+            assert dD.shape == D.shape and dQ.shape == Q.shape
+
+
+def pin_backward_finite_difference(orc):
+    """Central differences of L = sum_b g_b score_b on dyadic fp32 inputs whose argmax is
+    unique by a margin: L is linear in Q (and in D) near the point, every value is exact
+    in double, so (L(x + eV) - L(x - eV)) / 2e equals <grad, V> exactly."""
+    rng = np.random.default_rng(23)
+    q_len, nd, d, B = 5, 6, 8, 7
+    for _ in range(100):
+        Q = (rng.integers(-8, 9, size=(q_len, d)) / 8.0).astype(np.float32)
+        D = (rng.integers(-8, 9, size=(B, nd, d)) / 8.0).astype(np.float32)
+        S = np.einsum("ik,bjk->bij", Q.astype(np.float64), D.astype(np.float64))
+        top2 = np.sort(S, axis=2)[:, :, -2:]
+        if np.all(top2[:, :, 1] - top2[:, :, 0] >= 1.0 / 64):
+            break
+    else:
+        raise AssertionError("no input with a unique argmax margin")
+    g = (rng.integers(-4, 5, size=B) / 4.0).astype(np.float32)
+    _, _, ta = orc.maxsim_argmax(Q, D, "fp32")
+    dQ, dD = orc.maxsim_backward(Q, D, "fp32", ta, g)
+    eps = 2.0 ** -12
+
+    def L(Qx, Dx):
+        return float(np.sum(g.astype(np.float64) * orc.maxsim_fixed(Qx, Dx, "fp32")))
+
+    for _ in range(4):
+        V = rng.integers(-1, 2, size=Q.shape).astype(np.float32)
+        fd = (L(Q + eps * V, D) - L(Q - eps * V, D)) / (2 * eps)
+        assert fd == float(np.sum(dQ * V)), ("dQ", fd, float(np.sum(dQ * V)))
+        W = rng.integers(-1, 2, size=D.shape).astype(np.float32)
+        fd = (L(Q, D + eps * W) - L(Q, D - eps * W)) / (2 * eps)
+        assert fd == float(np.sum(dD * W)), ("dD", fd, float(np.sum(dD * W)))
+
+
+def pin_backward_one_token_docs(orc):
+    """Documents of one token: every query token picks it, so dD[b, 0] = g_b sum_i q_i
+    and dQ[i] = sum_b g_b d_b (closed form, for every i)."""
+    rng = np.random.default_rng(24)
+    Q = store(_unit_rows(rng, 5, 64), "bf16")
+    D = store(_unit_rows(rng, 9, 64), "bf16").reshape(9, 1, 64)
+    g = rng.standard_normal(9).astype(np.float32)
+    _, _, ta = orc.maxsim_argmax(Q, D, "bf16")
+    assert np.all(ta == 0)
+    dQ, dD = orc.maxsim_backward(Q, D, "bf16", ta, g)
+    qd, Dd = dec(Q, "bf16"), dec(D, "bf16")[:, 0]
+    assert np.allclose(dD[:, 0], np.outer(g, qd.sum(axis=0)), rtol=0, atol=1e-12)
+    assert np.allclose(dQ, np.broadcast_to(g.astype(np.float64) @ Dd, dQ.shape), rtol=0, atol=1e-12)
+
+
 PINS = [
     pin_golden_dense, pin_golden_int8, pin_golden_pq,
     pin_brute_dense, pin_brute_fp16_subnormal, pin_brute_int8, pin_brute_pq,
     pin_dyadic_self, pin_one_token_doc, pin_one_query_token, pin_one_hot,
     pin_doc_permutation_and_duplicates, pin_padding_and_neighbours, pin_power_of_two_scaling,
     pin_query_permutation, pin_planted_top10,
+    pin_argmax_brute, pin_backward_euler, pin_backward_finite_difference,
+    pin_backward_one_token_docs,
 ]

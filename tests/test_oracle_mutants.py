@@ -13,7 +13,8 @@ import oracle
 import oracle_pins
 
 MUTANTS = [
-    ("max_becomes_sum", "if (s > m) m = s;", "m = (m == -INFINITY ? 0.0 : m) + s;"),
+    ("max_becomes_sum", "if (s > m) { /* strict: the first maximum is kept */\n        m = s;",
+     "{\n        m = (m == -INFINITY ? 0.0 : m) + s;"),
     ("max_init_zero", "double m = -INFINITY;", "double m = 0.0;"),
     ("drop_last_doc_token", "for (int64_t j = 0; j < len; j++) {\n      double s = 0.0;\n      for (int k",
      "for (int64_t j = 0; j < len - 1; j++) {\n      double s = 0.0;\n      for (int k"),
@@ -48,6 +49,18 @@ MUTANTS = [
      "(double)C[((int64_t)k * M + m) * dsub + t]"),
     ("pq_code_index", "c->codes[(first + j) * c->M + m]", "c->codes[(first + m) * c->M + j]"),
     ("pq_max_init_zero", "double mx = -INFINITY;", "double mx = 0.0;"),
+    ("argmax_ties_to_highest", "if (s > m) { /* strict: the first", "if (s >= m) { /* strict: the first"),
+    ("argmax_off_by_one", "m = s;\n        arg = (int32_t)j;", "m = s;\n        arg = (int32_t)j + 1;"),
+    ("bwd_drop_grad", "const double g = (double)grad[b];", "const double g = 1.0;"),
+    ("bwd_dD_sign", "dD[(first + j) * d + k] += g", "dD[(first + j) * d + k] -= g"),
+    ("bwd_dD_wrong_row", "dD[(first + j) * d + k] += g", "dD[(first + (j + 1) % len) * d + k] += g"),
+    ("bwd_dQ_wrong_row", "g * decode(D, dtype, (first + j) * d + k)",
+     "g * decode(D, dtype, (first + (len - 1 - j)) * d + k)"),
+    ("bwd_dQ_transposed", "dQ[(int64_t)i * d + k] += g", "dQ[(int64_t)k * q_len + i] += g"),
+    ("bwd_skip_first_query", "for (int i = 0; i < q_len; i++) {\n      const int64_t j",
+     "for (int i = 1; i < q_len; i++) {\n      const int64_t j"),
+    ("bwd_tok_arg_transposed", "const int64_t j = tok_arg[b * q_len + i];",
+     "const int64_t j = tok_arg[(int64_t)i * n_docs + b];"),
 ]
 
 
