@@ -30,6 +30,7 @@
 #ifndef MAXSIM_H
 #define MAXSIM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -88,6 +89,51 @@ int maxsim_score(const void *Q, int q_len, const void *D, const int64_t *doc_off
  */
 int maxsim_score_fixed(const void *Q, int q_len, const void *D, int64_t n_docs, int nd,
                        const int32_t *doc_lens, int d, int dtype, float *out, void *stream);
+
+/*
+ * Scores with per-token maxima and argmax, for the backward pass (Flash-MaxSim
+ * abstract and page: training reuses the forward's argmax locations).
+ *   Q, D, d, dtype as for maxsim_score; doc_offsets nullable: CSR as in
+ *            maxsim_score, or NULL for fixed documents D [n_docs][nd][d] (nd >= 1)
+ *   out      fp32 [n_docs] scores, exactly as maxsim_score / maxsim_score_fixed
+ *   tok_max  fp32 [n_docs][q_len]: max_j <q_i, d_j> (the fp32 value the score sums)
+ *   tok_arg  int32 [n_docs][q_len]: the lowest j whose fp32 similarity equals that
+ *            maximum; an empty document gives -inf and -1.
+ * Both outputs are required. Sizes supported as for maxsim_score.
+ */
+int maxsim_score_argmax(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
+                        int64_t n_docs, int nd, int d, int dtype, float *out, float *tok_max,
+                        int32_t *tok_arg, void *stream);
+
+/*
+ * Backward pass: gradients of L = sum_b grad_out[b] * out[b] given the forward argmax
+ * (Flash-MaxSim abstract and page: backward through the argmax; inverse-grid CSR with
+ * an atomic-free, destination-owned reduction):
+ *     dD[b][j] = grad_out[b] * sum of q_i over the query tokens i with tok_arg[b][i] == j
+ *                (zero where no query token chose j)
+ *     dQ[i]    = sum_b grad_out[b] * D[b][tok_arg[b][i]]
+ *   Q, D, doc_offsets / nd, d, dtype  as for maxsim_score_argmax
+ *   tok_arg    int32 [n_docs][q_len] from maxsim_score_argmax (an entry outside
+ *              [0, len_b), such as the -1 of an empty document, contributes nothing)
+ *   grad_out   fp32 [n_docs]
+ *   grad_dtype type of dQ and dD: MAXSIM_FP32, or dtype itself (each value rounded
+ *              once, to nearest even, from its fp32 sum)
+ *   dQ         nullable [q_len][d] in grad_dtype: written when set (needs the workspace)
+ *   dD         nullable [tokens][d] in grad_dtype: every row of every document is
+ *              written when set; rows of tokens outside all documents are left untouched
+ *   workspace  device buffer of at least maxsim_backward_workspace_size(q_len, d,
+ *              n_docs) bytes, 16-byte aligned, when dQ is set (NULL otherwise); its
+ *              contents on entry do not matter
+ * The result does not depend on the run: every output element has one writer and a
+ * fixed summation order. dQ and dD are 16-byte aligned.
+ */
+int maxsim_backward(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
+                    int64_t n_docs, int nd, int d, int dtype, const int32_t *tok_arg,
+                    const float *grad_out, void *dQ, void *dD, int grad_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Workspace bytes maxsim_backward needs for dQ (0 for invalid sizes or n_docs == 0). */
+size_t maxsim_backward_workspace_size(int q_len, int d, int64_t n_docs);
 
 /*
  * INT8 x INT8 scoring with per-token fp32 scales (Flash-MaxSim abstract:

@@ -50,11 +50,16 @@ def lib() -> ctypes.CDLL:
         L.maxsim_score_i8.argtypes = [vp, vp, i32, vp, vp, vp, i64, i32, i32, vp, vp, vp, vp]
         L.maxsim_pq_tables.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, vp]
         L.maxsim_score_pq.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp]
+        L.maxsim_score_argmax.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
+        L.maxsim_backward.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
+                                      vp, ctypes.c_size_t, vp]
+        L.maxsim_backward_workspace_size.argtypes = [i32, i32, i64]
+        L.maxsim_backward_workspace_size.restype = ctypes.c_size_t
         L.maxsim_status_string.argtypes = [i32]
         L.maxsim_status_string.restype = ctypes.c_char_p
         L.maxsim_version.argtypes = []
         for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
-                  "maxsim_score_pq", "maxsim_version"):
+                  "maxsim_score_pq", "maxsim_version", "maxsim_score_argmax", "maxsim_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -142,6 +147,101 @@ def maxsim_score_i8(Q: torch.Tensor, q_scale: torch.Tensor, D: torch.Tensor,
                                  n_docs, nd, d, _dev(out, "out"), _dev(tm, "tok_max"),
                                  _dev(ta, "tok_arg"), _stream(stream)), "maxsim_score_i8")
     return (out, tm, ta) if with_token_max else out
+
+
+def _docs(D: torch.Tensor, doc_offsets):
+    """(n_docs, nd) of fixed documents D [n_docs, nd, d] or CSR tokens D [n_tokens, d]."""
+    if doc_offsets is None:
+        return D.shape[0], D.shape[1]
+    return doc_offsets.numel() - 1, 0
+
+
+def maxsim_score_argmax(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor | None = None,
+                        out=None, tok_max=None, tok_arg=None, stream=None):
+    """Scores with per-token maxima and argmax (lowest index on ties). Fixed layout
+    (D [n_docs, nd, d]) when doc_offsets is None, else CSR (D [n_tokens, d]). Returns
+    (scores fp32 [n_docs], tok_max fp32 [n_docs, q_len], tok_arg int32 [n_docs, q_len])."""
+    if D.dtype != Q.dtype:
+        raise ValueError("Q and D must share a dtype")
+    q_len, d = Q.shape
+    n_docs, nd = _docs(D, doc_offsets)
+    out = _out(out, n_docs, Q.device)
+    if tok_max is None:
+        tok_max = torch.empty((n_docs, q_len), dtype=torch.float32, device=Q.device)
+    if tok_arg is None:
+        tok_arg = torch.empty((n_docs, q_len), dtype=torch.int32, device=Q.device)
+    _check(lib().maxsim_score_argmax(_dev(Q, "Q"), q_len, _dev(D, "D"),
+                                     _dev(doc_offsets, "doc_offsets"), n_docs, nd, d,
+                                     _dtype_code(Q), _dev(out, "out"), _dev(tok_max, "tok_max"),
+                                     _dev(tok_arg, "tok_arg"), _stream(stream)),
+           "maxsim_score_argmax")
+    return out, tok_max, tok_arg
+
+
+def backward_workspace_size(q_len: int, d: int, n_docs: int) -> int:
+    """Bytes of workspace maxsim_backward needs to produce dQ."""
+    return int(lib().maxsim_backward_workspace_size(q_len, d, n_docs))
+
+
+def maxsim_backward(Q: torch.Tensor, D: torch.Tensor, tok_arg: torch.Tensor,
+                    grad_out: torch.Tensor, doc_offsets: torch.Tensor | None = None,
+                    want_dQ: bool = True, want_dD: bool = True, grad_dtype=torch.float32,
+                    dQ=None, dD=None, workspace=None, stream=None):
+    """Gradients of sum_b grad_out[b] * score_b from the forward argmax tok_arg. Returns
+    (dQ [q_len, d], dD shaped like D), each None when not asked for; grad_dtype is float32
+    or the dtype of Q and D."""
+    if D.dtype != Q.dtype:
+        raise ValueError("Q and D must share a dtype")
+    if grad_dtype not in (torch.float32, Q.dtype):
+        raise ValueError("grad_dtype must be float32 or the dtype of Q")
+    q_len, d = Q.shape
+    n_docs, nd = _docs(D, doc_offsets)
+    if want_dQ and dQ is None:
+        dQ = torch.empty((q_len, d), dtype=grad_dtype, device=Q.device)
+    if want_dD and dD is None:
+        dD = torch.empty(D.shape, dtype=grad_dtype, device=Q.device)
+    if not want_dQ:
+        dQ = None
+    if not want_dD:
+        dD = None
+    ws_bytes = 0
+    if dQ is not None:
+        ws_bytes = backward_workspace_size(q_len, d, n_docs)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
+    _check(lib().maxsim_backward(_dev(Q, "Q"), q_len, _dev(D, "D"), _dev(doc_offsets, "doc_offsets"),
+                                 n_docs, nd, d, _dtype_code(Q), _dev(tok_arg, "tok_arg"),
+                                 _dev(grad_out, "grad_out"), _dev(dQ, "dQ"), _dev(dD, "dD"),
+                                 _TORCH_DTYPE[grad_dtype], _dev(workspace, "workspace"), ws_bytes,
+                                 _stream(stream)), "maxsim_backward")
+    return dQ, dD
+
+
+class MaxSimFunction(torch.autograd.Function):
+    """Differentiable MaxSim scores: the forward keeps the argmax, the backward turns it
+    into dQ and dD with the library's kernels (gradients in the input dtype)."""
+
+    @staticmethod
+    def forward(ctx, Q, D, doc_offsets):
+        scores, _, tok_arg = maxsim_score_argmax(Q, D, doc_offsets)
+        ctx.save_for_backward(Q, D, doc_offsets, tok_arg)
+        return scores
+
+    @staticmethod
+    def backward(ctx, grad_scores):
+        Q, D, doc_offsets, tok_arg = ctx.saved_tensors
+        dQ, dD = maxsim_backward(Q, D, tok_arg, grad_scores.float().contiguous(), doc_offsets,
+                                 want_dQ=ctx.needs_input_grad[0], want_dD=ctx.needs_input_grad[1],
+                                 grad_dtype=Q.dtype)
+        return dQ, dD, None
+
+
+def maxsim(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor | None = None):
+    """Scores [n_docs] that autograd can differentiate with respect to Q and D."""
+    return MaxSimFunction.apply(Q, D, doc_offsets)
 
 
 def maxsim_pq_tables(Q: torch.Tensor, C: torch.Tensor, T: torch.Tensor | None = None,

@@ -1,0 +1,106 @@
+// libmaxsim backward entry points (include/maxsim.h): gradients of sum_b g_b * score_b
+// from the forward argmax.
+#include <hip/hip_runtime.h>
+
+#include "backward_kernel.hpp"
+#include "host_common.hpp"
+
+using namespace maxsim;
+
+namespace {
+
+template <int DT, int OT>
+int launch_dd(const BwdArgs &a, const DeviceInfo &di, hipStream_t st) {
+  auto kern = bwd_dd_kernel<DT, OT>;
+  const int bpc = blocks_per_cu((const void *)kern, BWD_THREADS, 0);
+  const int64_t max_wg = (int64_t)bpc * di.cus;
+  const int64_t need = (a.n_docs + BWD_WAVES - 1) / BWD_WAVES;
+  int64_t grid = need < max_wg ? need : max_wg;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), 0, st, a);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+template <int DT, int OT>
+int launch_dq(const BwdArgs &a, hipStream_t st) {
+  const int chunks = a.q_len * (a.d / 4);
+  const unsigned blocks = (unsigned)((chunks + DQ_CHUNKS_PER_WG - 1) / DQ_CHUNKS_PER_WG);
+  hipLaunchKernelGGL(bwd_dq_partial_kernel<DT>, dim3(blocks, (unsigned)a.n_ranges),
+                     dim3(BWD_THREADS), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
+  const int n_elem = a.q_len * a.d;
+  const unsigned rblocks = (unsigned)((n_elem + BWD_THREADS - 1) / BWD_THREADS);
+  hipLaunchKernelGGL(bwd_dq_reduce_kernel<OT>, dim3(rblocks), dim3(BWD_THREADS), 0, st,
+                     (const float *)a.partial, a.n_ranges, n_elem, a.dQ);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+int run_dd(const BwdArgs &a, int dtype, int grad_dtype, const DeviceInfo &di, hipStream_t st) {
+  const bool f32 = grad_dtype == MAXSIM_FP32;
+  switch (dtype) {
+  case MAXSIM_BF16:
+    return f32 ? launch_dd<DT_BF16, DT_FP32>(a, di, st) : launch_dd<DT_BF16, DT_BF16>(a, di, st);
+  case MAXSIM_FP16:
+    return f32 ? launch_dd<DT_FP16, DT_FP32>(a, di, st) : launch_dd<DT_FP16, DT_FP16>(a, di, st);
+  case MAXSIM_FP32: return launch_dd<DT_FP32, DT_FP32>(a, di, st);
+  }
+  return MAXSIM_ERR_DTYPE;
+}
+
+int run_dq(const BwdArgs &a, int dtype, int grad_dtype, hipStream_t st) {
+  const bool f32 = grad_dtype == MAXSIM_FP32;
+  switch (dtype) {
+  case MAXSIM_BF16:
+    return f32 ? launch_dq<DT_BF16, DT_FP32>(a, st) : launch_dq<DT_BF16, DT_BF16>(a, st);
+  case MAXSIM_FP16:
+    return f32 ? launch_dq<DT_FP16, DT_FP32>(a, st) : launch_dq<DT_FP16, DT_FP16>(a, st);
+  case MAXSIM_FP32: return launch_dq<DT_FP32, DT_FP32>(a, st);
+  }
+  return MAXSIM_ERR_DTYPE;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t maxsim_backward_workspace_size(int q_len, int d, int64_t n_docs) {
+  if (q_len < 1 || q_len > MAXSIM_MAX_Q_LEN || d < MAXSIM_MIN_D || d > MAXSIM_MAX_D ||
+      d % 32 != 0 || n_docs < 1)
+    return 0;
+  return (size_t)bwd_dq_ranges(q_len, d, n_docs) * (size_t)q_len * (size_t)d * sizeof(float);
+}
+
+int maxsim_backward(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
+                    int64_t n_docs, int nd, int d, int dtype, const int32_t *tok_arg,
+                    const float *grad_out, void *dQ, void *dD, int grad_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  if (elem_bytes(dtype) == 0) return MAXSIM_ERR_DTYPE;
+  if (grad_dtype != MAXSIM_FP32 && grad_dtype != dtype) return MAXSIM_ERR_DTYPE;
+  if (n_docs < 0 || q_len < 1 || q_len > MAXSIM_MAX_Q_LEN) return MAXSIM_ERR_SHAPE;
+  if (d < MAXSIM_MIN_D || d > MAXSIM_MAX_D || d % 32 != 0) return MAXSIM_ERR_SHAPE;
+  if (!doc_offsets && nd < 1) return MAXSIM_ERR_SHAPE;
+  if (!Q || !D || !tok_arg || !grad_out) return MAXSIM_ERR_NULL;
+  if (dQ && !workspace) return MAXSIM_ERR_NULL;
+  if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(tok_arg, 4) || !aligned(grad_out, 4) ||
+      (doc_offsets && !aligned(doc_offsets, 8)) || (dQ && !aligned(dQ, 16)) ||
+      (dD && !aligned(dD, 16)) || (workspace && !aligned(workspace, 16)))
+    return MAXSIM_ERR_ALIGN;
+  if (n_docs == 0 || (!dQ && !dD)) return MAXSIM_OK;
+  if (dQ && workspace_bytes < maxsim_backward_workspace_size(q_len, d, n_docs))
+    return MAXSIM_ERR_SHAPE;
+  DeviceInfo di;
+  int rc = current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  BwdArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs, doc_offsets ? 0 : nd, d,
+            tok_arg, grad_out, (char *)dQ, (char *)dD, (float *)workspace,
+            bwd_dq_ranges(q_len, d, n_docs)};
+  hipStream_t st = (hipStream_t)stream;
+  if (dD) {
+    rc = run_dd(a, dtype, grad_dtype, di, st);
+    if (rc != MAXSIM_OK) return rc;
+  }
+  if (dQ) return run_dq(a, dtype, grad_dtype, st);
+  return MAXSIM_OK;
+}
+
+}  // extern "C"

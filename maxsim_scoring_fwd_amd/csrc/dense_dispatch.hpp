@@ -13,5 +13,12 @@ int dense_dispatch_fp16(bool qlds, int ksb, int qb, const DenseArgs &a, size_t l
                         const DeviceInfo &di, hipStream_t st);
 int dense_dispatch_fp32(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
                         const DeviceInfo &di, hipStream_t st);
+// The same kernels writing per-token maxima and argmax (DenseArgs::tok_max / tok_arg).
+int dense_argmax_dispatch_bf16(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                               const DeviceInfo &di, hipStream_t st);
+int dense_argmax_dispatch_fp16(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                               const DeviceInfo &di, hipStream_t st);
+int dense_argmax_dispatch_fp32(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
+                               const DeviceInfo &di, hipStream_t st);
 
 }  // namespace maxsim

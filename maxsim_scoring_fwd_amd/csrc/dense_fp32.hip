@@ -5,7 +5,7 @@ namespace maxsim {
 
 int dense_dispatch_fp32(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds,
                         const DeviceInfo &di, hipStream_t st) {
-  return dense_by_mode<DT_FP32>(qlds, ksb, qb, a, lds, di, st);
+  return dense_by_mode<DT_FP32, false>(qlds, ksb, qb, a, lds, di, st);
 }
 
 }  // namespace maxsim

@@ -39,6 +39,11 @@
 //    one VGPR per 16-query block (Flash-MaxSim Figure 1: running max m, fp32
 //    accumulator). At the document's end, two cross-lane max steps and a
 //    16-lane sum give the score; one lane stores it.
+//  * With ARG the kernel also writes each query token's maximum and the lowest
+//    document index reaching it (the argmax the Flash-MaxSim backward pass
+//    reuses): rows are folded in increasing order with a strict comparison, and
+//    the row groups combine with ties going to the lower index, so a clamped
+//    duplicate row past the end never wins over the token it copies.
 #pragma once
 
 #include "device_common.hpp"
@@ -55,6 +60,8 @@ struct DenseArgs {
   const int32_t *doc_lens; // fixed layout: valid tokens per document, or nullptr
   int n_dblk;              // number of d blocks (1 when Q is in VGPRs)
   float *out;
+  float *tok_max;          // ARG only: per-token maxima [n_docs][q_len]
+  int32_t *tok_arg;        // ARG only: per-token argmax [n_docs][q_len]
 };
 
 constexpr int DENSE_THREADS = 256;
@@ -124,13 +131,14 @@ __device__ __forceinline__ int64_t wave_lower_bound(const int64_t *off, int64_t 
 // load in flight before each tile, which serialises the ring.
 struct Slot {
   int64_t doc;
-  int dblk;
+  int dblk, tile;
   bool valid, first_blk, last_blk, doc_end, empty;
 };
 
 // DT: storage type; KSB: 64-byte chunks per d block; QB: 16-query blocks;
-// P: tiles in flight per wave; QLDS: query operand read from LDS; LM: load mode.
-template <int DT, int KSB, int QB, int P, bool QLDS, int LM>
+// P: tiles in flight per wave; QLDS: query operand read from LDS; LM: load mode;
+// ARG: also write per-token maxima and argmax.
+template <int DT, int KSB, int QB, int P, bool QLDS, int LM, bool ARG>
 __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int PPR = KSB * 4;  // 16-byte pieces per row of one d block
@@ -203,7 +211,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       sl.doc = pb;
       bool advance = true;
       if (plen == 0) {
-        sl.dblk = 0;
+        sl.dblk = sl.tile = 0;
         sl.first_blk = sl.last_blk = sl.doc_end = sl.empty = true;
       } else {
         const int64_t t0 = ptile * 16;
@@ -212,6 +220,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         base = a.D + (pfirst + t0) * RB + (int64_t)pk * KSB * 64;
         const int64_t ntiles = (plen + 15) >> 4;
         sl.dblk = pk;
+        sl.tile = (int)ptile;
         sl.empty = false;
         sl.first_blk = (pk == 0);
         sl.last_blk = (pk == n_dblk - 1);
@@ -252,9 +261,11 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
 
   f32x4_t acc[QB];
   float m[QB];
+  int arg[ARG ? QB : 1];
 #pragma unroll
   for (int qb = 0; qb < QB; qb++) {
     m[qb] = -__builtin_inff();
+    if constexpr (ARG) arg[qb] = -1;
     acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
@@ -297,17 +308,51 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         }
       }
       if (slot[p].last_blk) {
+        if constexpr (ARG) {
+          // lane holds rows 4g .. 4g + 3 of the tile, in increasing order
+          const int row0 = slot[p].tile * 16 + 4 * g;
 #pragma unroll
-        for (int qb = 0; qb < QB; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
+          for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+              if (acc[qb][r] > m[qb]) {
+                m[qb] = acc[qb][r];
+                arg[qb] = row0 + r;
+              }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
+        }
       }
       if (slot[p].doc_end) {
         float s = 0.f;
 #pragma unroll
         for (int qb = 0; qb < QB; qb++) {
           float v = m[qb];
-          v = __builtin_fmaxf(v, __shfl_xor(v, 16));
-          v = __builtin_fmaxf(v, __shfl_xor(v, 32));
-          if (qb * 16 + r16 < q_len) s += v;
+          const int qi = qb * 16 + r16;
+          if constexpr (ARG) {
+            int j = arg[qb];
+#pragma unroll
+            for (int sh = 16; sh <= 32; sh <<= 1) {
+              const float ov = __shfl_xor(v, sh);
+              const int oj = __shfl_xor(j, sh);
+              if (ov > v || (ov == v && oj < j)) {
+                v = ov;
+                j = oj;
+              }
+            }
+            if (g == 0 && qi < q_len) {
+              // an empty document's slot multiplied dummy data: report no token
+              const int64_t o = slot[p].doc * q_len + qi;
+              a.tok_max[o] = slot[p].empty ? -__builtin_inff() : v;
+              a.tok_arg[o] = slot[p].empty ? -1 : j;
+            }
+            arg[qb] = -1;
+          } else {
+            v = __builtin_fmaxf(v, __shfl_xor(v, 16));
+            v = __builtin_fmaxf(v, __shfl_xor(v, 32));
+          }
+          if (qi < q_len) s += v;
           m[qb] = -__builtin_inff();
         }
         s += __shfl_xor(s, 1);

@@ -6,9 +6,9 @@
 namespace maxsim {
 namespace {
 
-template <int DT, int KSB, int QB, int P, bool QLDS, int LM>
+template <int DT, int KSB, int QB, int P, bool QLDS, int LM, bool ARG>
 int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStream_t st) {
-  auto kern = dense_maxsim_kernel<DT, KSB, QB, P, QLDS, LM>;
+  auto kern = dense_maxsim_kernel<DT, KSB, QB, P, QLDS, LM, ARG>;
   const size_t lds = q_lds + (LM == LOAD_STAGED ? DENSE_WAVES * stage_tile_bytes<KSB>() : 0);
   if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
   const int bpc = blocks_per_cu((const void *)kern, DENSE_THREADS, lds);
@@ -27,72 +27,72 @@ template <int KSB> constexpr bool stageable() { return (KSB & (KSB - 1)) == 0; }
 // depths 4 to 10 are within 1% of each other; 4 needs the fewest registers).
 template <int KSB> constexpr int default_depth() { return KSB <= 2 ? 8 : 4; }
 
-template <int DT, int KSB, int QB, bool QLDS>
+template <int DT, int KSB, int QB, bool QLDS, bool ARG>
 int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipStream_t st) {
   constexpr int LM = stageable<KSB>() ? LOAD_STAGED : LOAD_DIRECT;
-  if constexpr (DT == DT_BF16 && KSB == 4 && QB == 2) {
+  if constexpr (DT == DT_BF16 && KSB == 4 && QB == 2 && !ARG) {
     // The ColBERT shape (d = 128, 32 query tokens): load mode, ring depth and query
     // placement selectable for measurements.
     static const int depth = env_knob("MAXSIM_DENSE_DEPTH", 0);
     static const int mode = env_knob("MAXSIM_DENSE_LOAD", LM);
     if constexpr (!QLDS) {
       if (mode == LOAD_DIRECT) {
-        if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_DIRECT>(a, lds, di, st);
-        return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT>(a, lds, di, st);
+        if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_DIRECT, ARG>(a, lds, di, st);
+        return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT, ARG>(a, lds, di, st);
       }
       if (mode == LOAD_DIRECT_NT)
-        return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT_NT>(a, lds, di, st);
+        return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT_NT, ARG>(a, lds, di, st);
     }
-    if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LOAD_STAGED>(a, lds, di, st);
-    if (depth == 6) return launch_dense<DT, KSB, QB, 6, QLDS, LOAD_STAGED>(a, lds, di, st);
-    if (depth == 10) return launch_dense<DT, KSB, QB, 10, QLDS, LOAD_STAGED>(a, lds, di, st);
-    if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED>(a, lds, di, st);
+    if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
+    if (depth == 6) return launch_dense<DT, KSB, QB, 6, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
+    if (depth == 10) return launch_dense<DT, KSB, QB, 10, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
+    if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
   }
   if constexpr (LM == LOAD_STAGED) {
     // Where Q already fills LDS, the transpose buffers may not fit: load directly.
     if (lds + DENSE_WAVES * stage_tile_bytes<KSB>() > di.max_lds)
-      return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LOAD_DIRECT>(a, lds, di, st);
+      return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LOAD_DIRECT, ARG>(a, lds, di, st);
   }
-  return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LM>(a, lds, di, st);
+  return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LM, ARG>(a, lds, di, st);
 }
 
-template <int DT, int KSB, bool QLDS>
+template <int DT, int KSB, bool QLDS, bool ARG>
 int dense_by_qb(int qb, const DenseArgs &a, size_t lds, const DeviceInfo &di, hipStream_t st) {
   // Register-resident queries only while Q needs at most 64 VGPRs.
   switch (qb) {
-  case 1: return dense_with_depth<DT, KSB, 1, QLDS>(a, lds, di, st);
-  case 2: return dense_with_depth<DT, KSB, 2, QLDS>(a, lds, di, st);
+  case 1: return dense_with_depth<DT, KSB, 1, QLDS, ARG>(a, lds, di, st);
+  case 2: return dense_with_depth<DT, KSB, 2, QLDS, ARG>(a, lds, di, st);
   case 3:
-    if constexpr (QLDS || KSB * 3 <= 16) return dense_with_depth<DT, KSB, 3, QLDS>(a, lds, di, st);
+    if constexpr (QLDS || KSB * 3 <= 16) return dense_with_depth<DT, KSB, 3, QLDS, ARG>(a, lds, di, st);
     break;
   case 4:
-    if constexpr (QLDS || KSB * 4 <= 16) return dense_with_depth<DT, KSB, 4, QLDS>(a, lds, di, st);
+    if constexpr (QLDS || KSB * 4 <= 16) return dense_with_depth<DT, KSB, 4, QLDS, ARG>(a, lds, di, st);
     break;
   }
   return MAXSIM_ERR_UNSUPPORTED;
 }
 
-template <int DT, bool QLDS>
+template <int DT, bool QLDS, bool ARG>
 int dense_by_ksb(int ksb, int qb, const DenseArgs &a, size_t lds, const DeviceInfo &di,
                  hipStream_t st) {
   switch (ksb) {
-  case 1: return dense_by_qb<DT, 1, QLDS>(qb, a, lds, di, st);
-  case 2: return dense_by_qb<DT, 2, QLDS>(qb, a, lds, di, st);
-  case 3: return dense_by_qb<DT, 3, QLDS>(qb, a, lds, di, st);
-  case 4: return dense_by_qb<DT, 4, QLDS>(qb, a, lds, di, st);
-  case 5: return dense_by_qb<DT, 5, QLDS>(qb, a, lds, di, st);
-  case 6: return dense_by_qb<DT, 6, QLDS>(qb, a, lds, di, st);
-  case 7: return dense_by_qb<DT, 7, QLDS>(qb, a, lds, di, st);
-  case 8: return dense_by_qb<DT, 8, QLDS>(qb, a, lds, di, st);
+  case 1: return dense_by_qb<DT, 1, QLDS, ARG>(qb, a, lds, di, st);
+  case 2: return dense_by_qb<DT, 2, QLDS, ARG>(qb, a, lds, di, st);
+  case 3: return dense_by_qb<DT, 3, QLDS, ARG>(qb, a, lds, di, st);
+  case 4: return dense_by_qb<DT, 4, QLDS, ARG>(qb, a, lds, di, st);
+  case 5: return dense_by_qb<DT, 5, QLDS, ARG>(qb, a, lds, di, st);
+  case 6: return dense_by_qb<DT, 6, QLDS, ARG>(qb, a, lds, di, st);
+  case 7: return dense_by_qb<DT, 7, QLDS, ARG>(qb, a, lds, di, st);
+  case 8: return dense_by_qb<DT, 8, QLDS, ARG>(qb, a, lds, di, st);
   }
   return MAXSIM_ERR_UNSUPPORTED;
 }
 
-template <int DT>
+template <int DT, bool ARG>
 int dense_by_mode(bool qlds, int ksb, int qb, const DenseArgs &a, size_t lds, const DeviceInfo &di,
                   hipStream_t st) {
-  return qlds ? dense_by_ksb<DT, true>(ksb, qb, a, lds, di, st)
-              : dense_by_ksb<DT, false>(ksb, qb, a, lds, di, st);
+  return qlds ? dense_by_ksb<DT, true, ARG>(ksb, qb, a, lds, di, st)
+              : dense_by_ksb<DT, false, ARG>(ksb, qb, a, lds, di, st);
 }
 
 }  // namespace

@@ -15,8 +15,10 @@ using namespace maxsim;
 
 namespace {
 
-// Pick and launch the dense kernel for validated arguments.
+// Pick and launch the dense kernel for validated arguments; with tok_max / tok_arg set the
+// variant that also writes per-token maxima and argmax.
 int dense_run(DenseArgs a, int d, int dtype, hipStream_t st) {
+  const bool arg = a.tok_max != nullptr;
   DeviceInfo di;
   int rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
@@ -27,8 +29,8 @@ int dense_run(DenseArgs a, int d, int dtype, hipStream_t st) {
   if (qb > 4) {
     // Long queries: query slices across the waves of a workgroup.
     TiledArgs t{a.Q, a.q_len, a.D, a.offsets, a.n_docs, a.nd, a.doc_lens, nullptr, nullptr,
-                a.out, nullptr, nullptr};
-    return tiled_dense_run(t, d, dtype, di, st);
+                a.out, a.tok_max, a.tok_arg};
+    return arg ? tiled_dense_argmax_run(t, d, dtype, di, st) : tiled_dense_run(t, d, dtype, di, st);
   }
   bool qlds = force_lds || chunks > 8 || chunks * qb > 16;
   int ksb = chunks;
@@ -40,9 +42,15 @@ int dense_run(DenseArgs a, int d, int dtype, hipStream_t st) {
   size_t lds = qlds ? (size_t)qb * 16 * ((size_t)d * eb + 16) : 0;
   if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
   switch (dtype) {
-  case MAXSIM_BF16: return dense_dispatch_bf16(qlds, ksb, qb, a, lds, di, st);
-  case MAXSIM_FP16: return dense_dispatch_fp16(qlds, ksb, qb, a, lds, di, st);
-  case MAXSIM_FP32: return dense_dispatch_fp32(qlds, ksb, qb, a, lds, di, st);
+  case MAXSIM_BF16:
+    return arg ? dense_argmax_dispatch_bf16(qlds, ksb, qb, a, lds, di, st)
+               : dense_dispatch_bf16(qlds, ksb, qb, a, lds, di, st);
+  case MAXSIM_FP16:
+    return arg ? dense_argmax_dispatch_fp16(qlds, ksb, qb, a, lds, di, st)
+               : dense_dispatch_fp16(qlds, ksb, qb, a, lds, di, st);
+  case MAXSIM_FP32:
+    return arg ? dense_argmax_dispatch_fp32(qlds, ksb, qb, a, lds, di, st)
+               : dense_dispatch_fp32(qlds, ksb, qb, a, lds, di, st);
   }
   return MAXSIM_ERR_DTYPE;
 }
@@ -70,6 +78,21 @@ int maxsim_score_fixed(const void *Q, int q_len, const void *D, int64_t n_docs, 
   if (doc_lens && !aligned(doc_lens, 4)) return MAXSIM_ERR_ALIGN;
   if (n_docs == 0) return MAXSIM_OK;
   DenseArgs a{(const char *)Q, q_len, (const char *)D, nullptr, n_docs, nd, doc_lens, 1, out};
+  return dense_run(a, d, dtype, (hipStream_t)stream);
+}
+
+int maxsim_score_argmax(const void *Q, int q_len, const void *D, const int64_t *doc_offsets,
+                        int64_t n_docs, int nd, int d, int dtype, float *out, float *tok_max,
+                        int32_t *tok_arg, void *stream) {
+  int rc = check_dense(Q, q_len, D, n_docs, d, dtype, out);
+  if (rc != MAXSIM_OK) return rc;
+  if (!doc_offsets && nd < 1) return MAXSIM_ERR_SHAPE;
+  if (!tok_max || !tok_arg) return MAXSIM_ERR_NULL;
+  if ((doc_offsets && !aligned(doc_offsets, 8)) || !aligned(tok_max, 4) || !aligned(tok_arg, 4))
+    return MAXSIM_ERR_ALIGN;
+  if (n_docs == 0) return MAXSIM_OK;
+  DenseArgs a{(const char *)Q, q_len,   (const char *)D, doc_offsets, n_docs,
+              doc_offsets ? 0 : nd,   nullptr, 1,          out,         tok_max, tok_arg};
   return dense_run(a, d, dtype, (hipStream_t)stream);
 }
 

@@ -1,0 +1,21 @@
+// Query-tiled kernels for bf16 / fp16 / fp32 storage that also write per-token maxima
+// and argmax (queries longer than 64 tokens).
+#include "tiled_dispatch.hpp"
+
+namespace maxsim {
+
+int tiled_dense_argmax_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di,
+                           hipStream_t st) {
+  const int ksb = d * elem_bytes(dtype) / 64;
+  if (ksb != 1 && ksb != 2 && ksb != 4 && ksb != 8) return MAXSIM_ERR_UNSUPPORTED;
+  if (a.q_len > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
+  const int qbw = tiled_qbw(a.q_len);
+  switch (dtype) {
+  case MAXSIM_BF16: return tiled_by_ksb<DT_BF16, true>(ksb, qbw, a, di, st);
+  case MAXSIM_FP16: return tiled_by_ksb<DT_FP16, true>(ksb, qbw, a, di, st);
+  case MAXSIM_FP32: return tiled_by_ksb<DT_FP32, true>(ksb, qbw, a, di, st);
+  }
+  return MAXSIM_ERR_DTYPE;
+}
+
+}  // namespace maxsim

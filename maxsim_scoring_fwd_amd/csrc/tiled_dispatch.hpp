@@ -57,6 +57,9 @@ int tiled_by_ksb(int ksb, int qbw, const TiledArgs &a, const DeviceInfo &di, hip
 
 // Dense storage (bf16 / fp16 / fp32) with q_len > 64; defined in tiled_dense.hip.
 int tiled_dense_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di, hipStream_t st);
+// The same, also writing per-token maxima and argmax; defined in tiled_dense_arg.hip.
+int tiled_dense_argmax_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di,
+                           hipStream_t st);
 // INT8 storage; defined in tiled_i8.hip.
 int tiled_i8_run(const TiledArgs &a, int d, const DeviceInfo &di, hipStream_t st);
 

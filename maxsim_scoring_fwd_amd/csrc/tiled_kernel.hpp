@@ -21,7 +21,8 @@
 //  * Rows past the document's end are clamped to its last token (a duplicate
 //    cannot change a maximum); whole tiles past the end are skipped.
 //  * Per tile and query block, the 16x16 accumulator is reduced into a running
-//    max held in one VGPR per lane (plus the argmax for the INT8 token outputs).
+//    max held in one VGPR per lane (plus the argmax when per-token maxima and
+//    argmax are asked for: the lowest row reaching the maximum).
 //  * At the document's end each wave folds its maxima into one partial sum;
 //    the partials meet in LDS and one thread adds them in wave order. These sums
 //    over up to 1024 query tokens are taken in double and rounded once to fp32,
@@ -56,8 +57,8 @@ struct TiledArgs {
   const float *q_scale;     // int8 only
   const float *d_scale;     // int8 only, per document token
   float *out;
-  float *tok_max;           // int8 only, nullable: [n_docs][q_len]
-  int32_t *tok_arg;         // int8 only, nullable: [n_docs][q_len]
+  float *tok_max;           // ARG only: per-token maxima [n_docs][q_len]
+  int32_t *tok_arg;         // ARG only: per-token argmax [n_docs][q_len]
 };
 
 __device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int64_t &first,
@@ -78,7 +79,7 @@ __device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int6
 
 // DT: storage; KSB: 64-byte chunks per token row (d = KSB * 64 / element bytes);
 // QBW: 16-query blocks per wave (queries per workgroup = 8 * 16 * QBW);
-// ARG: also produce the per-token maxima and argmax (int8 only); NW: waves per workgroup.
+// ARG: also produce the per-token maxima and argmax; NW: waves per workgroup.
 template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES>
 __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   constexpr int TILED_THREADS = NW * WAVE;
@@ -259,8 +260,21 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
 #pragma unroll
             for (int qb = 0; qb < QBW; qb++)
               acc[qb] = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc[qb]);
+          if constexpr (ARG) {
+            // lane holds rows 4g .. 4g + 3 of the tile, in increasing order
+            const int row0 = blk * BLK_ROWS + t * 16 + 4 * g;
 #pragma unroll
-          for (int qb = 0; qb < QBW; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
+            for (int qb = 0; qb < QBW; qb++)
+#pragma unroll
+              for (int r = 0; r < 4; r++)
+                if (acc[qb][r] > m[qb]) {
+                  m[qb] = acc[qb][r];
+                  arg[qb] = row0 + r;
+                }
+          } else {
+#pragma unroll
+            for (int qb = 0; qb < QBW; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
+          }
         }
       }
     }

@@ -34,7 +34,8 @@ def declared_functions(header=HEADER):
 def test_header_declares_entry_points():
     names = declared_functions()
     for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
-              "maxsim_score_pq", "maxsim_status_string", "maxsim_version"):
+              "maxsim_score_pq", "maxsim_status_string", "maxsim_version", "maxsim_score_argmax",
+              "maxsim_backward", "maxsim_backward_workspace_size"):
         assert f in names
 
 
@@ -150,6 +151,53 @@ def test_pq_argument_errors(L):
     assert s(nd=0) == SHAPE
     assert s(codes=None) == NULL
     assert s(codes=P + 8) == ALIGN
+
+
+def test_argmax_argument_errors(L):
+    f = lambda **k: L.maxsim_score_argmax(k.get("Q", P), k.get("q_len", 32), k.get("D", P),
+                                          k.get("off", None), k.get("n", 5), k.get("nd", 16),
+                                          k.get("d", 128), k.get("dt", 0), k.get("out", P),
+                                          k.get("tm", P), k.get("ta", P), None)
+    assert f(tm=None) == NULL
+    assert f(ta=None) == NULL
+    assert f(out=None) == NULL
+    assert f(nd=0) == SHAPE
+    assert f(d=48) == SHAPE
+    assert f(dt=5) == DTYPE
+    assert f(tm=P + 2) == ALIGN
+    assert f(off=P + 4) == ALIGN
+    assert f(n=0) == OK
+
+
+def bwd(L, **k):
+    return L.maxsim_backward(k.get("Q", P), k.get("q_len", 32), k.get("D", P), k.get("off", None),
+                             k.get("n", 5), k.get("nd", 16), k.get("d", 128), k.get("dt", 0),
+                             k.get("ta", P), k.get("g", P), k.get("dQ", P), k.get("dD", P),
+                             k.get("gdt", 2), k.get("ws", P), k.get("wsb", 1 << 30), None)
+
+
+def test_backward_argument_errors(L):
+    assert bwd(L, ta=None) == NULL
+    assert bwd(L, g=None) == NULL
+    assert bwd(L, ws=None) == NULL          # dQ needs the workspace
+    assert bwd(L, gdt=1) == DTYPE           # bf16 data, fp16 gradients
+    assert bwd(L, dt=9) == DTYPE
+    assert bwd(L, q_len=1025) == SHAPE
+    assert bwd(L, nd=0) == SHAPE
+    assert bwd(L, wsb=1024) == SHAPE        # workspace too small
+    assert bwd(L, dD=P + 8) == ALIGN
+    assert bwd(L, ws=P + 4) == ALIGN
+    assert bwd(L, n=0) == OK
+    assert bwd(L, dQ=None, dD=None) == OK   # nothing asked for
+
+
+def test_backward_workspace_size(L):
+    f = L.maxsim_backward_workspace_size
+    # 32 x 128 dQ: one block of 4096 elements, 2048 document ranges of fp32 partial sums
+    assert f(32, 128, 100000) == 2048 * 32 * 128 * 4
+    assert f(32, 128, 10) == 10 * 32 * 128 * 4      # never more ranges than documents
+    assert f(1024, 128, 175000) == 64 * 1024 * 128 * 4
+    assert f(0, 128, 10) == 0 and f(32, 48, 10) == 0 and f(32, 128, 0) == 0
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
