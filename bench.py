@@ -32,7 +32,8 @@ LDS_PEAK_GBS = 256 * 128 * 2.4
 METRIC = "docs/s + % HBM peak, MaxSim B=100K Nq=32 Nd=128 d=128 bf16"
 
 # layout: fixed (D [B, nd, d]) or csr (lognormal lengths, median 70, sigma 0.5, 8..512).
-# path: dense (bf16/fp16/fp32), i8 (INT8 x INT8, per-token scales), pq (tables + lookups).
+# path: dense (bf16/fp16/fp32), i8 (INT8 x INT8, per-token scales), pq (tables + lookups),
+#       train (scores with argmax, then dQ and dD of sum_b g_b score_b in the input dtype).
 # pool: build the corpus from this many distinct seeded documents repeated to B.
 _CB = dict(layout="fixed", path="dense", q_len=32, nd=128, d=128, dtype="bf16", seed=2)
 WORKLOADS = {
@@ -63,6 +64,10 @@ WORKLOADS = {
     "csr-bf16": dict(_CB, B=100_000, layout="csr", seed=5),
     "csr-pq": dict(_CB, B=100_000, layout="csr", seed=5, path="pq"),
     "fixed-pq": dict(_CB, B=100_000, seed=5, path="pq"),
+    "train-colbert-b100k": dict(_CB, B=100_000, path="train"),
+    "train-csr": dict(_CB, B=100_000, layout="csr", seed=5, path="train"),
+    "train-colpali-b10k": dict(_CB, B=10_000, q_len=1024, nd=1024, seed=4, pool=2_048,
+                               path="train"),
 }
 DEFAULT = "colbert-b100k"
 # sources the dense bf16 kernel is built from (the kernel whose HBM traffic is stored)
@@ -92,6 +97,8 @@ def esize(dtype):
 
 
 def bound_of(w):
+    if w["path"] == "train":
+        return "hbm"  # the dD kernel: writes one gradient row per document token
     if w["path"] == "pq":
         return "lds"
     if w["path"] == "i8" or w["q_len"] > 64:
@@ -156,6 +163,8 @@ def make_inputs(w, device):
                 S[b0 * nd:b1 * nd] = S[0:(b1 - b0) * nd]
         inp["D"] = D.view(B, nd, d)
         inp["d_scale"] = S
+        if w["path"] == "train":
+            _train_buffers(w, inp, device)
         return inp
 
     lens = gen.lengths(seed, B)
@@ -173,13 +182,35 @@ def make_inputs(w, device):
     S = torch.empty(T, dtype=torch.float32, device=device) if dt == "i8" else None
     _fill_rows(D, seed, 0, T, d, dt, device, chunk_rows, S)
     inp["D"], inp["d_scale"] = D, S
+    if w["path"] == "train":
+        _train_buffers(w, inp, device)
     return inp
+
+
+def _train_buffers(w, inp, device):
+    """Outputs of the training step: per-token maxima and argmax, an upstream gradient
+    g_b ~ N(0, 1) per document (seeded), dQ and dD in the input dtype, the dQ workspace."""
+    import numpy as np
+    import torch
+
+    import maxsim_scoring_fwd_amd as ms
+    B, q, d = w["B"], w["q_len"], w["d"]
+    inp["tok_max"] = torch.empty((B, q), dtype=torch.float32, device=device)
+    inp["tok_arg"] = torch.empty((B, q), dtype=torch.int32, device=device)
+    g = np.random.default_rng(w["seed"]).standard_normal(B).astype(np.float32)
+    inp["grad"] = torch.from_numpy(g).to(device)
+    inp["dQ"] = torch.empty((q, d), dtype=inp["D"].dtype, device=device)
+    inp["dD"] = torch.empty(inp["D"].shape, dtype=inp["D"].dtype, device=device)
+    inp["workspace"] = torch.empty(max(16, ms.backward_workspace_size(q, d, B)), dtype=torch.uint8,
+                                   device=device)
 
 
 def work_per_launch(w, inp):
     """Algorithmic work of the dominant kernel per launch: (amount, unit of the rate)."""
     n_tok, q, d, B = inp["n_tokens"], w["q_len"], w["d"], w["B"]
     bound = bound_of(w)
+    if w["path"] == "train":
+        return train_dd_bytes(w, inp), "GB/s"
     if bound == "hbm":
         b = n_tok * d * esize(w["dtype"]) + q * d * esize(w["dtype"]) + B * 4
         if inp["offsets"] is not None:
@@ -190,16 +221,43 @@ def work_per_launch(w, inp):
     return n_tok * q * PQ_M * 4, "GB/s"  # fp32 table entries looked up
 
 
+def train_dd_bytes(w, inp):
+    """Algorithmic bytes of the dD kernel: every document token's gradient row written once
+    (input dtype), the argmax and the upstream gradient read once, the query read once, the
+    offsets of a CSR corpus."""
+    n_tok, q, d, B, e = inp["n_tokens"], w["q_len"], w["d"], w["B"], esize(w["dtype"])
+    b = n_tok * d * e + B * q * 4 + B * 4 + q * d * e
+    if inp["offsets"] is not None:
+        b += (B + 1) * 8
+    return b
+
+
 def hbm_bytes(w, inp):
     """Bytes every document token costs in HBM (for context on mfma / lds-bound paths)."""
     if w["path"] == "pq":
         return inp["n_tokens"] * PQ_M + w["B"] * 4
+    if w["path"] == "train":
+        # forward: D read, scores + per-token maxima and argmax written; dQ: the chosen rows
+        # gathered; dD: gradient rows written
+        e, q, d, B = esize(w["dtype"]), w["q_len"], w["d"], w["B"]
+        fwd = inp["n_tokens"] * d * e + B * 4 + B * q * 8
+        return fwd + B * q * (d * e + 4) + train_dd_bytes(w, inp)
     b = inp["n_tokens"] * (w["d"] * esize(w["dtype"]) + (4 if w["dtype"] == "i8" else 0))
     return b + w["B"] * 4
 
 
 def launches(ms, w, inp, out):
     """The kernel launches of one step, as (name, callable); the last one is dominant."""
+    if w["path"] == "train":
+        off, D = inp["offsets"], inp["D"]
+        fwd = lambda: ms.maxsim_score_argmax(inp["Q"], D, off, out=out, tok_max=inp["tok_max"],
+                                             tok_arg=inp["tok_arg"])
+        bwd = lambda q, dd: ms.maxsim_backward(inp["Q"], D, inp["tok_arg"], inp["grad"], off,
+                                               want_dQ=q, want_dD=dd, grad_dtype=D.dtype,
+                                               dQ=inp["dQ"], dD=inp["dD"],
+                                               workspace=inp["workspace"])
+        return [("maxsim_argmax", fwd), ("backward_dq", lambda: bwd(True, False)),
+                ("backward_dd", lambda: bwd(False, True))]
     if w["path"] == "pq":
         steps = [("pq_tables", lambda: ms.maxsim_pq_tables(inp["Q"], inp["C"], T=inp["T"]))]
         if inp["offsets"] is None:
@@ -252,9 +310,17 @@ def cpu_baseline(w, budget_s: float):
             return time.perf_counter() - t
         Qh = gen.tokens(seed, gen.S_QUERY, 0, q, d, dt)
         Dh = gen.tokens(seed, gen.S_DOCS, 0, n_tok, d, dt)
+        if off is None:
+            Dh = Dh.reshape(n, w["nd"], d)
+        if w["path"] == "train":
+            g = np.random.default_rng(seed).standard_normal(w["B"]).astype(np.float32)[:n]
+            t = time.perf_counter()
+            _, _, ta = oracle.maxsim_argmax(Qh, Dh, dt, offsets=off, nthreads=threads)
+            oracle.maxsim_backward(Qh, Dh, dt, ta, g, offsets=off)
+            return time.perf_counter() - t
         t = time.perf_counter()
         if off is None:
-            oracle.maxsim_fixed(Qh, Dh.reshape(n, w["nd"], d), dt, nthreads=threads)
+            oracle.maxsim_fixed(Qh, Dh, dt, nthreads=threads)
         else:
             oracle.maxsim_csr(Qh, Dh, off, dt, nthreads=threads)
         return time.perf_counter() - t
@@ -390,19 +456,27 @@ def main():
         buf = torch.empty(1 << 30, dtype=torch.int32, device=dev)  # 4 GiB
         buf.fill_(1)
         sink = torch.zeros(65536, dtype=torch.int32, device=dev)
-        for _ in range(3):
-            ms.calib_read(buf, sink)
-        cs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
-        ce = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
-        for i in range(10):
-            cs[i].record(stream)
-            ms.calib_read(buf, sink)
-            ce[i].record(stream)
-        torch.cuda.synchronize()
-        cal_ms = sorted(s.elapsed_time(e) for s, e in zip(cs, ce))[5]
-        stream_gbs = buf.numel() * 4 / (cal_ms * 1e-3) / 1e9
+        def median_ms(fn):
+            for _ in range(3):
+                fn()
+            cs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+            ce = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+            for i in range(10):
+                cs[i].record(stream)
+                fn()
+                ce[i].record(stream)
+            torch.cuda.synchronize()
+            return sorted(s.elapsed_time(e) for s, e in zip(cs, ce))[5]
+
+        stream_gbs = buf.numel() * 4 / (median_ms(lambda: ms.calib_read(buf, sink)) * 1e-3) / 1e9
         context["stream_read_GBps"] = round(stream_gbs, 1)
-        if bound == "hbm":
+        if w["path"] == "train":
+            # the dD kernel mostly writes: its ceiling is the streaming-write rate
+            wr_gbs = buf.numel() * 4 / (median_ms(lambda: ms.calib_write(buf)) * 1e-3) / 1e9
+            context["stream_write_GBps"] = round(wr_gbs, 1)
+            context["frac_of_stream_write"] = round(achieved / wr_gbs, 4)
+            log(f"stream-write ceiling {wr_gbs:.0f} GB/s")
+        elif bound == "hbm":
             context["frac_of_stream_read"] = round(achieved / stream_gbs, 4)
         del buf
         log(f"stream-read ceiling {stream_gbs:.0f} GB/s")
@@ -422,6 +496,9 @@ def main():
         cfg["lengths"] = "lognormal median 70 sigma 0.5 clipped 8..512"
     if w["path"] == "pq":
         cfg["pq"] = {"M": PQ_M, "K": PQ_K, "dsub": PQ_DSUB}
+    if w["path"] == "train":
+        cfg["step"] = ("scores with per-token argmax, then dQ and dD of sum_b g_b score_b "
+                       f"(g_b ~ N(0,1), gradients in {w['dtype']})")
     line = {
         "metric": METRIC if args.workload == DEFAULT else f"docs/s, MaxSim {args.workload}",
         "value": round(value, 1),

@@ -25,6 +25,10 @@ extern "C" {
 #endif
 
 int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+/* Streams `bytes` of a fixed pattern into dst with 128-bit stores (each wave writing whole
+ * 16 KiB blocks, one workgroup per CU): the achievable HBM write bandwidth, the ceiling
+ * of a kernel that mostly writes (the backward's dD). dst 16-byte aligned, bytes % 16 == 0. */
+int maxsim_calib_write(void *dst, size_t bytes, void *stream);
 int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /*

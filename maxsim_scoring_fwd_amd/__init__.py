@@ -280,6 +280,8 @@ def _calib_lib():
         vp = ctypes.c_void_p
         L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
         L.maxsim_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.maxsim_calib_write.argtypes = [vp, ctypes.c_size_t, vp]
+        L.maxsim_calib_write.restype = ctypes.c_int
         L.maxsim_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.maxsim_calib_read.restype = ctypes.c_int
         L.maxsim_calib_copy.restype = ctypes.c_int
@@ -292,6 +294,12 @@ def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
     """Stream-read every byte of src (achievable read bandwidth); sink: >= 65536 words."""
     _check(_calib_lib().maxsim_calib_read(_dev(src, "src"), src.numel() * src.element_size(),
                                           _dev(sink, "sink"), _stream(stream)), "maxsim_calib_read")
+
+
+def calib_write(dst: torch.Tensor, stream=None):
+    """Stream a fixed pattern into every byte of dst (achievable write bandwidth)."""
+    _check(_calib_lib().maxsim_calib_write(_dev(dst, "dst"), dst.numel() * dst.element_size(),
+                                           _stream(stream)), "maxsim_calib_write")
 
 
 def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

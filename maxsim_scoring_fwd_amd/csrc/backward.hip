@@ -9,27 +9,55 @@ using namespace maxsim;
 
 namespace {
 
-template <int DT, int OT>
-int launch_dd(const BwdArgs &a, const DeviceInfo &di, hipStream_t st) {
-  auto kern = bwd_dd_kernel<DT, OT>;
-  const int bpc = blocks_per_cu((const void *)kern, BWD_THREADS, 0);
+// Segment length of the inverse grid: a fixed-layout document in one segment where it
+// fits, CSR documents (unknown lengths on the host) in segments of 256 tokens.
+inline int dd_seg_cap(const BwdArgs &a) {
+  if (a.offsets) return 256;
+  const int r = (a.nd + WAVE - 1) / WAVE * WAVE;
+  return r < BWD_SEG ? r : BWD_SEG;
+}
+
+template <int DT, int OT, bool QLDS>
+int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di,
+                  hipStream_t st) {
+  // Workgroups per CU: fixed-length documents with the query in LDS write fastest from two
+  // workgroups per CU (measured 5.45 against 5.06 TB/s at as many as fit: fewer streams of
+  // stores); CSR documents and long queries need every resident wave to hide the latency
+  // of their per-document phases. Non-temporal stores: the gradient rows are not re-read
+  // (ordinary stores measured 0.1 ms slower per training step at the ColBERT shape). Knobs
+  // override both for measurements.
+  static const int nt = env_knob("MAXSIM_BWD_NT", 1);
+  static const int wgs = env_knob("MAXSIM_BWD_WGS", -1);
+  auto kern = nt ? bwd_dd_kernel<DT, OT, QLDS, true> : bwd_dd_kernel<DT, OT, QLDS, false>;
+  const size_t lds = (size_t)q_lds + (size_t)BWD_WAVES * bwd_dd_wave_ints(seg_cap, a.q_len) * 4;
+  if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
+  int bpc = blocks_per_cu((const void *)kern, BWD_THREADS, lds);
+  const int cap = wgs >= 0 ? wgs : (QLDS && !a.offsets ? 2 : 0);
+  if (cap > 0 && cap < bpc) bpc = cap;
   const int64_t max_wg = (int64_t)bpc * di.cus;
   const int64_t need = (a.n_docs + BWD_WAVES - 1) / BWD_WAVES;
   int64_t grid = need < max_wg ? need : max_wg;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), 0, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), lds, st, a, seg_cap, q_lds);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
 template <int DT, int OT>
+int launch_dd(const BwdArgs &a, const DeviceInfo &di, hipStream_t st) {
+  const int seg_cap = dd_seg_cap(a);
+  const int q_bytes = a.q_len * a.d * Elem<DT>::bytes;  // a multiple of 64 (d % 32 == 0)
+  if (q_bytes <= BWD_Q_LDS_MAX) return launch_dd_lds<DT, OT, true>(a, seg_cap, q_bytes, di, st);
+  return launch_dd_lds<DT, OT, false>(a, seg_cap, 0, di, st);
+}
+
+template <int DT, int OT>
 int launch_dq(const BwdArgs &a, hipStream_t st) {
-  const int chunks = a.q_len * (a.d / 4);
-  const unsigned blocks = (unsigned)((chunks + DQ_CHUNKS_PER_WG - 1) / DQ_CHUNKS_PER_WG);
+  const unsigned blocks = (unsigned)((a.q_len * a.d + DQ_ELEMS_PER_WG - 1) / DQ_ELEMS_PER_WG);
   hipLaunchKernelGGL(bwd_dq_partial_kernel<DT>, dim3(blocks, (unsigned)a.n_ranges),
                      dim3(BWD_THREADS), 0, st, a);
   if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
   const int n_elem = a.q_len * a.d;
-  const unsigned rblocks = (unsigned)((n_elem + BWD_THREADS - 1) / BWD_THREADS);
+  const unsigned rblocks = (unsigned)((n_elem + RED_ELEMS - 1) / RED_ELEMS);
   hipLaunchKernelGGL(bwd_dq_reduce_kernel<OT>, dim3(rblocks), dim3(BWD_THREADS), 0, st,
                      (const float *)a.partial, a.n_ranges, n_elem, a.dQ);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;

@@ -17,8 +17,9 @@
 //    (a stable placement: ranks among equal rows come from a scan of the 64
 //    lanes' keys, not from atomics). Each lane then writes 16-byte chunks of the
 //    rows; a chunk sums its row's query tokens in that fixed order and scales by
-//    g_b once. Long documents are processed in segments of BWD_SEG tokens. CSR
-//    documents are split into token-balanced contiguous ranges across waves.
+//    g_b once; the query is read from LDS when it fits. Long documents are processed
+//    in segments of at most BWD_SEG tokens. CSR documents are split into token-balanced
+//    contiguous ranges across waves.
 //  * dQ (gathers q_len document rows per document). Each workgroup owns a block
 //    of 4-element chunks of dQ and a contiguous range of documents, and adds
 //    g_b times the chosen rows in document order into registers; the partial
@@ -52,11 +53,10 @@ struct BwdArgs {
 
 constexpr int BWD_THREADS = 256;
 constexpr int BWD_WAVES = BWD_THREADS / WAVE;
-constexpr int BWD_SEG = 1024;  // document tokens per inverse-grid segment
-constexpr int BWD_MAX_Q = 1024;
-constexpr int DQ_SLOTS = 4;                              // 4-element dQ chunks per thread
-constexpr int DQ_CHUNKS_PER_WG = BWD_THREADS * DQ_SLOTS;  // 4096 dQ elements per workgroup
-constexpr int DQ_DOCS = 4;                               // documents in flight per step
+constexpr int BWD_SEG = 1024;  // longest inverse-grid segment (document tokens)
+constexpr int BWD_Q_LDS_MAX = 48 * 1024;  // largest query copied to LDS (bytes)
+constexpr int DQ_ELEMS_PER_WG = 4096;  // dQ elements per workgroup (16-byte chunks per thread)
+constexpr int DQ_DOCS = 4;             // documents in flight per step
 
 __device__ __forceinline__ void bwd_extent(const BwdArgs &a, int64_t b, int64_t &first,
                                            int64_t &len) {
@@ -110,14 +110,22 @@ __device__ __forceinline__ void load_f32(const char *p, float (&x)[E]) {
   }
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> 16-bit gradient bits, rounded to nearest even (gfx950 converts two values
+// per instruction).
+template <int OT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (OT == DT_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+  } else {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  }
 }
 
-// Store 16 bytes of output type OT (E = 16 / element bytes values), non-temporal.
-template <int OT, int E>
+// Store 16 bytes of output type OT (E = 16 / element bytes values); NT: non-temporal.
+template <int OT, int E, bool NT>
 __device__ __forceinline__ void store_chunk(char *p, const float (&x)[E]) {
   u32x4_t v;
   if constexpr (OT == DT_FP32) {
@@ -126,34 +134,58 @@ __device__ __forceinline__ void store_chunk(char *p, const float (&x)[E]) {
                 __float_as_uint(x[3])};
   } else {
     static_assert(E == 8, "16-bit chunk");
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++)
-      h[e] = OT == DT_BF16 ? bf16_rne(x[e])
-                           : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x[e]);
-    v = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    v = u32x4_t{pack2<OT>(x[0], x[1]), pack2<OT>(x[2], x[3]), pack2<OT>(x[4], x[5]),
+                pack2<OT>(x[6], x[7])};
   }
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+  else
+    *reinterpret_cast<u32x4_t *>(p) = v;
 }
 
-// dD: one wave per document; DT the storage type of Q and D, OT the gradient type.
-template <int DT, int OT>
-__global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a) {
-  __shared__ int32_t cnt_lds[BWD_WAVES][BWD_SEG];      // counts, then placement cursors
-  __shared__ int32_t off_lds[BWD_WAVES][BWD_SEG + 1];  // row starts of the inverse grid
-  __shared__ int32_t idx_lds[BWD_WAVES][BWD_MAX_Q];    // query tokens grouped by row
+// Dynamic LDS of the dD kernel: the query as stored (QLDS) at offset 0, then per wave
+// cnt[seg_cap], off[seg_cap + 1] and idx[q_len] (int32).
+__host__ __device__ inline int bwd_dd_wave_ints(int seg_cap, int q_len) {
+  return 2 * seg_cap + 1 + q_len;
+}
+
+// dD: one wave per document; DT the storage type of Q and D, OT the gradient type; QLDS:
+// the query is copied to LDS once per workgroup (when it fits), else read through L2.
+template <int DT, int OT, bool QLDS, bool NT>
+__global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a, int seg_cap,
+                                                             int q_lds_bytes) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int IB = Elem<DT>::bytes;
   constexpr int OB = Elem<OT>::bytes;
   constexpr int E = 16 / OB;  // gradient elements per 16-byte output chunk
   const int lane = threadIdx.x & (WAVE - 1);
   const int wv = threadIdx.x >> 6;
-  int32_t *cnt = cnt_lds[wv];
-  int32_t *off = off_lds[wv];
-  int32_t *idx = idx_lds[wv];
+  const int q_len = a.q_len, d = a.d;
+  if constexpr (QLDS) {
+    const int pieces = q_len * d * IB / 16;
+    for (int p = threadIdx.x; p < pieces; p += BWD_THREADS)
+      reinterpret_cast<u32x4_t *>(lds)[p] = load16(a.Q + (int64_t)p * 16);
+    __syncthreads();
+  }
+  int32_t *cnt =
+      reinterpret_cast<int32_t *>(lds + q_lds_bytes) + wv * bwd_dd_wave_ints(seg_cap, q_len);
+  int32_t *off = cnt + seg_cap;
+  int32_t *idx = off + seg_cap + 1;
   const int64_t wave = uniform((int64_t)blockIdx.x * BWD_WAVES + wv);
   const int64_t nwaves = (int64_t)gridDim.x * BWD_WAVES;
-  const int q_len = a.q_len;
-  const int cpr = a.d / E;  // output chunks per row
+  const int cpr = d / E;  // output chunks per row
+  // lanes -> (row, chunk): cpr divides 64 for d <= 256 (bf16 / fp16) and d <= 128 (fp32)
+  const bool by_row = WAVE % cpr == 0;
+  const int rpi = by_row ? WAVE / cpr : 0;
+  const int my_c = by_row ? lane % cpr : 0, my_r = by_row ? lane / cpr : 0;
+
+  auto q_chunk = [&](int i, int c, float (&x)[E]) {
+    const int64_t o = ((int64_t)i * d + c * E) * IB;
+    if constexpr (QLDS)
+      load_f32<DT, E>(lds + o, x);
+    else
+      load_f32<DT, E>(a.Q + o, x);
+  };
 
   // documents of this wave: a token-balanced contiguous range (CSR) or a stride
   int64_t b = wave, bend = a.n_docs, bstep = nwaves;
@@ -172,8 +204,8 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a) {
     bwd_extent(a, b, first, len);
     const float g = a.grad[b];
     const int32_t *arg = a.tok_arg + b * q_len;
-    for (int64_t s0 = 0; s0 < len; s0 += BWD_SEG) {
-      const int seg = (int)(len - s0 < BWD_SEG ? len - s0 : BWD_SEG);
+    for (int64_t s0 = 0; s0 < len; s0 += seg_cap) {
+      const int seg = (int)(len - s0 < seg_cap ? len - s0 : seg_cap);
       // 1. how many query tokens chose each row of the segment
       for (int j = lane; j < seg; j += WAVE) cnt[j] = 0;
       wave_lds_sync();
@@ -224,54 +256,61 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a) {
         if (key >= 0 && after == 0) cnt[key] += before + 1;  // the row's last lane
         wave_lds_sync();
       }
-      // 4. write the segment's rows; zero rows need no query reads
-      char *dst = a.dD + (first + s0) * (int64_t)a.d * OB;
-      const int nchunk = seg * cpr;
-      for (int u = lane; u < nchunk; u += WAVE) {
-        const int row = u / cpr, c = u - row * cpr;
+      // 4. write the segment's rows; a row nobody chose is zero and reads no query
+      char *dst = a.dD + (first + s0) * (int64_t)d * OB;
+      auto emit = [&](int row, int c) {
         const int e0 = off[row], e1 = off[row + 1];
         float acc[E];
 #pragma unroll
         for (int k = 0; k < E; k++) acc[k] = 0.f;
         for (int e = e0; e < e1; e++) {
           float x[E];
-          load_f32<DT, E>(a.Q + ((int64_t)idx[e] * a.d + c * E) * IB, x);
+          q_chunk(idx[e], c, x);
 #pragma unroll
           for (int k = 0; k < E; k++) acc[k] += x[k];
         }
 #pragma unroll
         for (int k = 0; k < E; k++) acc[k] *= g;
-        store_chunk<OT, E>(dst + (int64_t)u * 16, acc);
+        store_chunk<OT, E, NT>(dst + ((int64_t)row * cpr + c) * 16, acc);
+      };
+      if (by_row) {
+        for (int row = my_r; row < seg; row += rpi) emit(row, my_c);
+      } else {
+        for (int u = lane; u < seg * cpr; u += WAVE) emit(u / cpr, u % cpr);
       }
       wave_lds_sync();  // the next segment reuses the wave's LDS
     }
   }
 }
 
-// dQ partial sums: grid (chunk blocks, document ranges).
+// dQ partial sums: grid (element blocks, document ranges). Each thread owns SLOTS chunks
+// of 16 bytes of the stored type (E elements each) of dQ and adds g_b times the chosen
+// rows' chunks for the documents of its range, in document order.
 template <int DT>
 __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_partial_kernel(BwdArgs a) {
   constexpr int IB = Elem<DT>::bytes;
-  const int cpr = a.d / 4;
-  const int total = a.q_len * cpr;  // 4-element chunks of dQ
+  constexpr int E = 16 / IB;
+  constexpr int SLOTS = DQ_ELEMS_PER_WG / (BWD_THREADS * E);
+  const int cpr = a.d / E;
+  const int total = a.q_len * cpr;  // chunks of dQ
   const int r = blockIdx.y;
   const int64_t b0 = a.n_docs * r / a.n_ranges, b1 = a.n_docs * (r + 1) / a.n_ranges;
-  int qi[DQ_SLOTS], cc[DQ_SLOTS];
-  bool ok[DQ_SLOTS];
-  float acc[DQ_SLOTS][4];
+  int qi[SLOTS], cc[SLOTS];
+  bool ok[SLOTS];
+  float acc[SLOTS][E];
 #pragma unroll
-  for (int s = 0; s < DQ_SLOTS; s++) {
-    const int u = blockIdx.x * DQ_CHUNKS_PER_WG + s * BWD_THREADS + threadIdx.x;
+  for (int s = 0; s < SLOTS; s++) {
+    const int u = blockIdx.x * (BWD_THREADS * SLOTS) + s * BWD_THREADS + threadIdx.x;
     ok[s] = u < total;
     qi[s] = ok[s] ? u / cpr : 0;
     cc[s] = ok[s] ? u - qi[s] * cpr : 0;
 #pragma unroll
-    for (int k = 0; k < 4; k++) acc[s][k] = 0.f;
+    for (int k = 0; k < E; k++) acc[s][k] = 0.f;
   }
   for (int64_t bb = b0; bb < b1; bb += DQ_DOCS) {
     int64_t first[DQ_DOCS], len[DQ_DOCS];
     float g[DQ_DOCS];
-    int j[DQ_DOCS][DQ_SLOTS];
+    int j[DQ_DOCS][SLOTS];
 #pragma unroll
     for (int t = 0; t < DQ_DOCS; t++) {
       const int64_t b = bb + t;
@@ -283,58 +322,71 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_partial_kernel(BwdArgs a) 
         g[t] = a.grad[b];
       }
 #pragma unroll
-      for (int s = 0; s < DQ_SLOTS; s++)
+      for (int s = 0; s < SLOTS; s++)
         j[t][s] = (b < b1 && ok[s]) ? a.tok_arg[b * a.q_len + qi[s]] : -1;
     }
     // documents in order, so each chunk's sum has a fixed order
 #pragma unroll
     for (int t = 0; t < DQ_DOCS; t++)
 #pragma unroll
-      for (int s = 0; s < DQ_SLOTS; s++) {
+      for (int s = 0; s < SLOTS; s++) {
         if (j[t][s] >= 0 && j[t][s] < len[t]) {
-          float x[4];
-          load_f32<DT, 4>(a.D + ((first[t] + j[t][s]) * a.d + cc[s] * 4) * IB, x);
+          float x[E];
+          load_f32<DT, E>(a.D + ((first[t] + j[t][s]) * a.d + cc[s] * E) * IB, x);
 #pragma unroll
-          for (int k = 0; k < 4; k++) acc[s][k] = __builtin_fmaf(g[t], x[k], acc[s][k]);
+          for (int k = 0; k < E; k++) acc[s][k] = __builtin_fmaf(g[t], x[k], acc[s][k]);
         }
       }
   }
-  float *dst = a.partial + (int64_t)r * total * 4;
+  float *dst = a.partial + (int64_t)r * total * E;
 #pragma unroll
-  for (int s = 0; s < DQ_SLOTS; s++) {
-    const int u = blockIdx.x * DQ_CHUNKS_PER_WG + s * BWD_THREADS + threadIdx.x;
-    if (ok[s])
-      *reinterpret_cast<f32x4_t *>(dst + (int64_t)u * 4) =
-          f32x4_t{acc[s][0], acc[s][1], acc[s][2], acc[s][3]};
+  for (int s = 0; s < SLOTS; s++) {
+    const int u = blockIdx.x * (BWD_THREADS * SLOTS) + s * BWD_THREADS + threadIdx.x;
+    if (ok[s]) {
+#pragma unroll
+      for (int h = 0; h < E / 4; h++)
+        *reinterpret_cast<f32x4_t *>(dst + (int64_t)u * E + 4 * h) =
+            f32x4_t{acc[s][4 * h], acc[s][4 * h + 1], acc[s][4 * h + 2], acc[s][4 * h + 3]};
+    }
   }
 }
 
-// dQ[e] = sum over ranges of the partial sums, in range order, in double; stored in the
-// gradient type OT (rounded once, to nearest even).
+// dQ[e] = sum over ranges of the partial sums in double; stored in the gradient type OT
+// (rounded once, to nearest even). A workgroup takes RED_ELEMS consecutive elements; its
+// RED_GROUPS thread groups each add every RED_GROUPS-th range in increasing order, and the
+// group sums are added in group order: a fixed order, whatever the timing.
+constexpr int RED_ELEMS = 16;
+constexpr int RED_GROUPS = BWD_THREADS / RED_ELEMS;
 template <int OT>
 __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_reduce_kernel(const float *partial,
                                                                     int n_ranges, int n_elem,
                                                                     char *dQ) {
-  const int e = blockIdx.x * BWD_THREADS + threadIdx.x;
-  if (e >= n_elem) return;
+  __shared__ double red[RED_GROUPS][RED_ELEMS];
+  const int el = threadIdx.x % RED_ELEMS, grp = threadIdx.x / RED_ELEMS;
+  const int e = blockIdx.x * RED_ELEMS + el;
   double s = 0.0;
-  for (int r = 0; r < n_ranges; r++) s += (double)partial[(int64_t)r * n_elem + e];
-  const float f = (float)s;
+  if (e < n_elem) {
+#pragma unroll 8
+    for (int r = grp; r < n_ranges; r += RED_GROUPS) s += (double)partial[(int64_t)r * n_elem + e];
+  }
+  red[grp][el] = s;
+  __syncthreads();
+  if (grp != 0 || e >= n_elem) return;
+  double tot = 0.0;
+  for (int k = 0; k < RED_GROUPS; k++) tot += red[k][el];
+  const float f = (float)tot;
   if constexpr (OT == DT_FP32)
     reinterpret_cast<float *>(dQ)[e] = f;
-  else if constexpr (OT == DT_BF16)
-    reinterpret_cast<uint16_t *>(dQ)[e] = (uint16_t)bf16_rne(f);
   else
-    reinterpret_cast<_Float16 *>(dQ)[e] = (_Float16)f;
+    reinterpret_cast<uint16_t *>(dQ)[e] = (uint16_t)(pack2<OT>(f, 0.f) & 0xffffu);
 }
 
 // Document ranges of the dQ partial sums: enough workgroups to fill the device
-// (about 2048 with the chunk blocks), never more ranges than documents. A function
+// (about 2048 with the element blocks), never more ranges than documents. A function
 // of the sizes only, so the workspace and the summation order do not depend on
 // the device.
 inline int bwd_dq_ranges(int q_len, int d, int64_t n_docs) {
-  const int chunks = q_len * (d / 4);
-  const int blocks = (chunks + DQ_CHUNKS_PER_WG - 1) / DQ_CHUNKS_PER_WG;
+  const int blocks = (q_len * d + DQ_ELEMS_PER_WG - 1) / DQ_ELEMS_PER_WG;
   int64_t r = 2048 / blocks;
   if (r < 1) r = 1;
   if (r > n_docs) r = n_docs;

@@ -148,16 +148,17 @@ class Oracle:
                                                _threads(nthreads)), "maxsim_argmax")
         return out, tm, ta
 
-    def maxsim_backward(self, Q, D, dtype: str, tok_arg, grad, offsets=None):
+    def maxsim_backward(self, Q, D, dtype: str, tok_arg, grad, offsets=None, want_dQ=True,
+                        want_dD=True):
         """Gradients of sum_b grad[b] * score_b for the argmax tok_arg [n_docs, q_len].
-        Returns (dQ f64 [q_len, d], dD f64 shaped like D)."""
+        Returns (dQ f64 [q_len, d], dD f64 shaped like D), None for an output not asked for."""
         Q, D = _c(Q), _c(D)
         n_docs, nd, off = self._layout(D, offsets)
         q_len, d = Q.shape
         ta = _c(tok_arg, np.int32).reshape(n_docs, q_len)
         g = _c(grad, np.float32).reshape(n_docs)
-        dQ = np.empty((q_len, d), dtype=np.float64)
-        dD = np.empty(D.shape, dtype=np.float64)
+        dQ = np.empty((q_len, d), dtype=np.float64) if want_dQ else None
+        dD = np.empty(D.shape, dtype=np.float64) if want_dD else None
         self._rc(self.lib.oracle_maxsim_backward(_ptr(Q), q_len, _ptr(D), _ptr(off), n_docs, nd, d,
                                                  DTYPES[dtype], _ptr(ta), _ptr(g), _ptr(dQ),
                                                  _ptr(dD)), "maxsim_backward")

@@ -210,19 +210,19 @@ int oracle_maxsim_argmax(const void *Q, int q_len, const void *D, const int64_t 
 }
 
 /* Gradients of sum_b grad[b] * score_b given the argmax tok_arg[n_docs][q_len]:
- * dQ[q_len][d] and dD[n_tokens][d] (n_tokens = offsets[n_docs], or n_docs * nd), in double.
+ * dQ[q_len][d] and dD[n_tokens][d] (n_tokens = offsets[n_docs], or n_docs * nd), in double;
+ * either output may be NULL (not computed).
  * An argmax outside [0, len_b) (the -1 of an empty document) contributes nothing. */
 int oracle_maxsim_backward(const void *Q, int q_len, const void *D, const int64_t *offsets,
                            int64_t n_docs, int nd, int d, int dtype, const int32_t *tok_arg,
                            const float *grad, double *dQ, double *dD) {
-  if (!Q || !D || !tok_arg || !grad || !dQ || !dD || q_len < 0 || d <= 0 || n_docs < 0)
-    return -1;
+  if (!Q || !D || !tok_arg || !grad || q_len < 0 || d <= 0 || n_docs < 0) return -1;
   if (!offsets && nd < 0) return -1;
   if (dtype < OR_BF16 || dtype > OR_FP32) return -1;
   double *q = decode_query(Q, q_len, d, dtype);
   const int64_t n_tokens = offsets ? offsets[n_docs] : n_docs * (int64_t)nd;
-  memset(dQ, 0, sizeof(double) * (size_t)q_len * (size_t)d);
-  memset(dD, 0, sizeof(double) * (size_t)n_tokens * (size_t)d);
+  if (dQ) memset(dQ, 0, sizeof(double) * (size_t)q_len * (size_t)d);
+  if (dD) memset(dD, 0, sizeof(double) * (size_t)n_tokens * (size_t)d);
   for (int64_t b = 0; b < n_docs; b++) {
     const int64_t first = offsets ? offsets[b] : b * (int64_t)nd;
     const int64_t len = offsets ? offsets[b + 1] - offsets[b] : nd;
@@ -231,8 +231,8 @@ int oracle_maxsim_backward(const void *Q, int q_len, const void *D, const int64_
       const int64_t j = tok_arg[b * q_len + i];
       if (j < 0 || j >= len) continue;
       for (int k = 0; k < d; k++) {
-        dQ[(int64_t)i * d + k] += g * decode(D, dtype, (first + j) * d + k);
-        dD[(first + j) * d + k] += g * q[(int64_t)i * d + k];
+        if (dQ) dQ[(int64_t)i * d + k] += g * decode(D, dtype, (first + j) * d + k);
+        if (dD) dD[(first + j) * d + k] += g * q[(int64_t)i * d + k];
       }
     }
   }

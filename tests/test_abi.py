@@ -49,7 +49,8 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_calibration_symbols_are_exported(L):
     names = declared_functions(CALIB_HEADER)
-    assert {"maxsim_calib_read", "maxsim_calib_copy", "maxsim_calib_mfma"} <= set(names)
+    assert {"maxsim_calib_read", "maxsim_calib_copy", "maxsim_calib_mfma",
+            "maxsim_calib_write"} <= set(names)
     out = os.popen(f"nm -D --defined-only {ms.LIB_PATH}").read()
     assert set(names) <= set(re.findall(r" T (maxsim_\w+)", out))
 

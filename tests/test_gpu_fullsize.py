@@ -118,3 +118,76 @@ def test_pq_every_document(name):
         codes = gen.codes(w["seed"], w["B"] * w["nd"], bench.PQ_M, bench.PQ_K)
         want = oracle.maxsim_pq(T, codes, nd=w["nd"])
     compare(got, want, tol=PQ_TOL, what=f"{name} (all docs)")
+
+
+def _argmax_rule(Q, docs_of_ids, ids, ta_gpu, ta_orc, tm_orc, margin):
+    """Where the GPU argmax differs from the oracle's, the GPU's token must be within
+    `margin` of the maximum (a near-tie that fp32 rounding may decide either way)."""
+    diff = np.argwhere(ta_gpu[ids] != ta_orc[ids])
+    for k, i in diff:
+        b = ids[k]
+        row = docs_of_ids(b)[ta_gpu[b, i]]
+        assert float(row @ Q[i]) >= tm_orc[b, i] - margin, (b, i, ta_gpu[b, i], ta_orc[b, i])
+    return len(diff)
+
+
+@pytest.mark.parametrize("name", ["train-colbert-b100k", "train-csr"])
+def test_train_step_full_size(name):
+    """The training step at the headline shape: forward scores, per-token maxima and argmax
+    on every document; then the backward, given the oracle's argmax in the same launch
+    configuration: dQ element by element, dD on sampled documents."""
+    import torch
+
+    from oracle_pins import dec
+    from test_gpu_backward import check_bound
+    w, inp, got = run(name)
+    ta_gpu = inp["tok_arg"].cpu().numpy()
+    tm_gpu = inp["tok_max"].cpu().numpy().astype(np.float64)
+    if w["layout"] == "fixed":
+        c = gen.fixed_corpus(w["seed"], w["B"], w["q_len"], w["nd"], w["d"], w["dtype"])
+        Dd = lambda b: dec(c.D[b], w["dtype"])
+    else:
+        c = gen.csr_corpus(w["seed"], w["B"], w["q_len"], w["d"], w["dtype"])
+        Dd = lambda b: dec(c.D[c.offsets[b]:c.offsets[b + 1]], w["dtype"])
+    ws, tm, ta = oracle.maxsim_argmax(c.Q, c.D, w["dtype"], offsets=c.offsets)
+    compare(got, ws, what=f"{name} scores (all docs)")
+    assert np.abs(tm_gpu - tm).max() <= 2e-5
+    Qd = dec(c.Q, w["dtype"])
+    nd = _argmax_rule(Qd, Dd, np.arange(w["B"]), ta_gpu, ta, tm, 2e-5)
+    say(f"  {name}: argmax differs from the oracle's on {nd} of {ta.size} near-tied pairs")
+
+    # backward from the oracle's argmax, same entry point and buffers as the step
+    g = inp["grad"].cpu().numpy()
+    inp["tok_arg"].copy_(torch.from_numpy(ta))
+    ms().maxsim_backward(inp["Q"], inp["D"], inp["tok_arg"], inp["grad"], inp["offsets"],
+                         grad_dtype=inp["D"].dtype, dQ=inp["dQ"], dD=inp["dD"],
+                         workspace=inp["workspace"])
+    torch.cuda.synchronize()
+    gQ = inp["dQ"].float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(7)
+    ids = np.unique(np.concatenate([[0, w["B"] - 1], rng.integers(0, w["B"], size=400)]))
+    if w["layout"] == "fixed":
+        gD = inp["dD"][torch.from_numpy(ids).cuda()].float().cpu().numpy().astype(np.float64)
+    else:
+        rows = np.concatenate([np.arange(c.offsets[b], c.offsets[b + 1]) for b in ids])
+        gD = inp["dD"][torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    n_ranges = ms().backward_workspace_size(w["q_len"], w["d"], w["B"]) // (w["q_len"] * w["d"] * 4)
+    release(inp)
+
+    absQ, absD = c.Q & 0x7fff, c.D & 0x7fff  # bf16 |x|: clear the sign bit
+    dQ, _ = oracle.maxsim_backward(c.Q, c.D, w["dtype"], ta, g, offsets=c.offsets, want_dD=False)
+    mQ, _ = oracle.maxsim_backward(absQ, absD, w["dtype"], ta, np.abs(g), offsets=c.offsets,
+                                   want_dD=False)
+    per_range = -(-w["B"] // n_ranges)
+    check_bound(gQ, dQ, mQ, per_range, w["dtype"], f"{name} dQ")
+    # dD rows of the sampled documents depend only on those documents
+    if w["layout"] == "fixed":
+        sub, soff = c.D[ids], None
+    else:
+        lens = c.offsets[ids + 1] - c.offsets[ids]
+        soff = gen.csr_offsets(lens)
+        sub = c.D[rows]
+    dD = oracle.maxsim_backward(c.Q, sub, w["dtype"], ta[ids], g[ids], offsets=soff)[1]
+    mD = oracle.maxsim_backward(absQ, sub & 0x7fff, w["dtype"], ta[ids], np.abs(g[ids]),
+                                offsets=soff)[1]
+    check_bound(gD, dD, mD, w["q_len"], w["dtype"], f"{name} dD ({len(ids)} sampled docs)")
