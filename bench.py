@@ -70,9 +70,14 @@ WORKLOADS = {
                                path="train"),
 }
 DEFAULT = "colbert-b100k"
-# sources the dense bf16 kernel is built from (the kernel whose HBM traffic is stored)
-KERNEL_SOURCES = ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "dense_variants.hpp",
-                  "dense_dispatch.hpp", "dense_bf16.hip"]
+# sources each stored traffic reading depends on: the dense bf16 kernel (headline) and the
+# backward's dD kernel (training step)
+KERNEL_SOURCES = {
+    "dense": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "dense_variants.hpp",
+              "dense_dispatch.hpp", "dense_bf16.hip"],
+    "train": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "backward_kernel.hpp",
+              "backward.hip"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PQ_M, PQ_K, PQ_DSUB = 16, 256, 8
 
@@ -81,12 +86,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel sources and compile flags, to tell whether stored counter readings
-    still apply to the kernels that run."""
+def kernel_hash(path: str = "dense") -> str:
+    """Hash of a kernel's sources and the compile flags, to tell whether stored counter
+    readings still apply to the kernel that runs."""
     from maxsim_scoring_fwd_amd import build
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES.get(path, KERNEL_SOURCES["dense"]):
         h.update(open(os.path.join(ROOT, "maxsim_scoring_fwd_amd", "csrc", f), "rb").read())
     h.update(" ".join(build.HIP_FLAGS[:-2]).encode())  # flags without the include path
     return h.hexdigest()[:16]
@@ -442,14 +447,14 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
-        if rec and rec.get("kernel_hash") == kernel_hash():
+        if rec and rec.get("kernel_hash") == kernel_hash(w["path"]):
             traffic = rec.get("bytes_per_launch")
 
     context = {"dominant_kernel": steps_fns[-1][0], "kernel_ms_avg": round(avg_dom, 5),
                "kernel_ms_min": round(min(dom_ms), 5), "work_per_launch": work,
                "hbm_bytes_per_step": footprint,
                "hbm_GBps": round(footprint / (avg_step * 1e-3) / 1e9, 1),
-               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash()}
+               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash(w["path"])}
     if w.get("pool") and w["pool"] < w["B"]:
         context["pool"] = f"{w['pool']} distinct documents repeated to {w['B']}"
     if not args.no_calib:
