@@ -91,6 +91,21 @@ int maxsim_score_fixed(const void *Q, int q_len, const void *D, int64_t n_docs, 
                        const int32_t *doc_lens, int d, int dtype, float *out, void *stream);
 
 /*
+ * Several queries against the same documents in one pass over them (each document byte
+ * read once per group of queries; TileMaxSim deep reading, section 2 item (1): tiling
+ * along queries as well): out[q][b] = sum_i max_j <Q[q][i], d_j>.
+ *   Q        [n_q][q_len][d] in `dtype`, n_q >= 1
+ *   D, doc_offsets / nd, d, dtype  as for maxsim_score_argmax (CSR, or fixed when NULL)
+ *   out      fp32 [n_q][n_docs]
+ * Queries are padded to whole 16-token blocks and grouped so that a group holds at most
+ * 1024 * 64 / (d * element bytes) (at most 1024) padded tokens; each group is one launch.
+ * Needs d * element bytes to be 64, 128, 256 or 512, else MAXSIM_ERR_UNSUPPORTED.
+ */
+int maxsim_score_batch(const void *Q, int n_q, int q_len, const void *D,
+                       const int64_t *doc_offsets, int64_t n_docs, int nd, int d, int dtype,
+                       float *out, void *stream);
+
+/*
  * Scores with per-token maxima and argmax, for the backward pass (Flash-MaxSim
  * abstract and page: training reuses the forward's argmax locations).
  *   Q, D, d, dtype as for maxsim_score; doc_offsets nullable: CSR as in

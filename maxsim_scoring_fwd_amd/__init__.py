@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
         L.maxsim_pq_tables.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, vp]
         L.maxsim_score_pq.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, vp, vp]
         L.maxsim_score_argmax.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
+        L.maxsim_score_batch.argtypes = [vp, i32, i32, vp, vp, i64, i32, i32, i32, vp, vp]
         L.maxsim_backward.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp, i32,
                                       vp, ctypes.c_size_t, vp]
         L.maxsim_backward_workspace_size.argtypes = [i32, i32, i64]
@@ -59,7 +60,8 @@ def lib() -> ctypes.CDLL:
         L.maxsim_status_string.restype = ctypes.c_char_p
         L.maxsim_version.argtypes = []
         for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
-                  "maxsim_score_pq", "maxsim_version", "maxsim_score_argmax", "maxsim_backward"):
+                  "maxsim_score_pq", "maxsim_version", "maxsim_score_argmax", "maxsim_backward",
+                  "maxsim_score_batch"):
             getattr(L, f).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -176,6 +178,24 @@ def maxsim_score_argmax(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Ten
                                      _dev(tok_arg, "tok_arg"), _stream(stream)),
            "maxsim_score_argmax")
     return out, tok_max, tok_arg
+
+
+def maxsim_score_batch(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor | None = None,
+                       out=None, stream=None) -> torch.Tensor:
+    """Several queries in one pass over the documents. Q [n_q, q_len, d]; fixed documents
+    D [n_docs, nd, d] when doc_offsets is None, else CSR D [n_tokens, d]. Returns fp32 scores
+    [n_q, n_docs]."""
+    if D.dtype != Q.dtype:
+        raise ValueError("Q and D must share a dtype")
+    n_q, q_len, d = Q.shape
+    n_docs, nd = _docs(D, doc_offsets)
+    if out is None:
+        out = torch.empty((n_q, n_docs), dtype=torch.float32, device=Q.device)
+    _check(lib().maxsim_score_batch(_dev(Q, "Q"), n_q, q_len, _dev(D, "D"),
+                                    _dev(doc_offsets, "doc_offsets"), n_docs, nd, d,
+                                    _dtype_code(Q), _dev(out, "out"), _stream(stream)),
+           "maxsim_score_batch")
+    return out
 
 
 def backward_workspace_size(q_len: int, d: int, n_docs: int) -> int:

@@ -96,6 +96,34 @@ int maxsim_score_argmax(const void *Q, int q_len, const void *D, const int64_t *
   return dense_run(a, d, dtype, (hipStream_t)stream);
 }
 
+int maxsim_score_batch(const void *Q, int n_q, int q_len, const void *D,
+                       const int64_t *doc_offsets, int64_t n_docs, int nd, int d, int dtype,
+                       float *out, void *stream) {
+  int rc = check_dense(Q, q_len, D, n_docs, d, dtype, out);
+  if (rc != MAXSIM_OK) return rc;
+  if (n_q < 1 || (!doc_offsets && nd < 1)) return MAXSIM_ERR_SHAPE;
+  if (doc_offsets && !aligned(doc_offsets, 8)) return MAXSIM_ERR_ALIGN;
+  const int ksb = d * elem_bytes(dtype) / 64;
+  if (d * elem_bytes(dtype) % 64 != 0 || (ksb != 1 && ksb != 2 && ksb != 4 && ksb != 8))
+    return MAXSIM_ERR_UNSUPPORTED;
+  const int q_pad = (q_len + 15) & ~15;
+  const int group = tiled_max_q(ksb) / q_pad;  // queries per pass over the documents
+  if (group < 1) return MAXSIM_ERR_UNSUPPORTED;
+  if (n_docs == 0) return MAXSIM_OK;
+  DeviceInfo di;
+  rc = current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  const int64_t q_bytes = (int64_t)q_len * d * elem_bytes(dtype);
+  for (int q0 = 0; q0 < n_q; q0 += group) {
+    TiledArgs a{(const char *)Q + q0 * q_bytes, q_len, (const char *)D, doc_offsets, n_docs,
+                doc_offsets ? 0 : nd, nullptr, nullptr, nullptr, out + (int64_t)q0 * n_docs,
+                nullptr, nullptr, n_q - q0 < group ? n_q - q0 : group};
+    rc = tiled_batch_run(a, d, dtype, di, (hipStream_t)stream);
+    if (rc != MAXSIM_OK) return rc;
+  }
+  return MAXSIM_OK;
+}
+
 int maxsim_score_i8(const int8_t *Q, const float *q_scale, int q_len, const int8_t *D,
                     const float *d_scale, const int64_t *doc_offsets, int64_t n_docs, int nd,
                     int d, float *out, float *tok_max, int32_t *tok_arg, void *stream) {

@@ -6,8 +6,8 @@ namespace maxsim {
 int tiled_dense_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di, hipStream_t st) {
   const int ksb = d * elem_bytes(dtype) / 64;
   if (ksb != 1 && ksb != 2 && ksb != 4 && ksb != 8) return MAXSIM_ERR_UNSUPPORTED;
-  if (a.q_len > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
-  const int qbw = tiled_qbw(a.q_len);
+  if (tiled_tokens(a) > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
+  const int qbw = tiled_qbw(tiled_tokens(a));
   // 16 waves of 4 query blocks each (measurement knob for the ColPali shape)
   static const int waves = env_knob("MAXSIM_TILED_WAVES", TILED_WAVES);
   if (waves == 16 && ksb == 4 && a.q_len > 768 && dtype == MAXSIM_BF16)

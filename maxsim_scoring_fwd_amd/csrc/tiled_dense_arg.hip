@@ -8,8 +8,8 @@ int tiled_dense_argmax_run(const TiledArgs &a, int d, int dtype, const DeviceInf
                            hipStream_t st) {
   const int ksb = d * elem_bytes(dtype) / 64;
   if (ksb != 1 && ksb != 2 && ksb != 4 && ksb != 8) return MAXSIM_ERR_UNSUPPORTED;
-  if (a.q_len > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
-  const int qbw = tiled_qbw(a.q_len);
+  if (tiled_tokens(a) > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
+  const int qbw = tiled_qbw(tiled_tokens(a));
   switch (dtype) {
   case MAXSIM_BF16: return tiled_by_ksb<DT_BF16, true>(ksb, qbw, a, di, st);
   case MAXSIM_FP16: return tiled_by_ksb<DT_FP16, true>(ksb, qbw, a, di, st);

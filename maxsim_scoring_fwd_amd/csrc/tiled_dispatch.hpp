@@ -6,16 +6,19 @@
 
 namespace maxsim {
 
-// Query blocks per wave for a query length (8 waves x 16 tokens x QBW >= q_len).
-inline int tiled_qbw(int q_len) { return (q_len + TILED_WAVES * 16 - 1) / (TILED_WAVES * 16); }
+// Query tokens of a launch: n_q queries, each padded to whole 16-token blocks.
+inline int tiled_tokens(const TiledArgs &a) { return a.n_q * ((a.q_len + 15) & ~15); }
+
+// Query blocks per wave for a number of query tokens (8 waves x 16 tokens x QBW >= tokens).
+inline int tiled_qbw(int tokens) { return (tokens + TILED_WAVES * 16 - 1) / (TILED_WAVES * 16); }
 
 // Largest query length the tiled kernel holds for KSB 64-byte chunks per row:
 // the slice of one wave needs QBW * KSB * 4 VGPRs, kept at or below 128.
 inline int tiled_max_q(int ksb) { return TILED_WAVES * 16 * (32 / ksb > 16 ? 16 : 32 / ksb); }
 
-template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES>
+template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES, bool BATCH = false>
 int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
-  auto kern = tiled_maxsim_kernel<DT, KSB, QBW, ARG, NW>;
+  auto kern = tiled_maxsim_kernel<DT, KSB, QBW, ARG, NW, BATCH>;
   const int bpc = blocks_per_cu((const void *)kern, NW * WAVE, 0);
   const int64_t max_wg = (int64_t)bpc * di.cus;
   int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
@@ -24,12 +27,13 @@ int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
-template <int DT, int KSB, bool ARG>
+template <int DT, int KSB, bool ARG, bool BATCH>
 int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   switch (qbw) {
 #define MAXSIM_TILED_CASE(N)                                                                      \
   case N:                                                                                         \
-    if constexpr (N * KSB <= 32) return launch_tiled<DT, KSB, N, ARG>(a, di, st);                 \
+    if constexpr (N * KSB <= 32)                                                                  \
+      return launch_tiled<DT, KSB, N, ARG, TILED_WAVES, BATCH>(a, di, st);                        \
     break;
     MAXSIM_TILED_CASE(1)
     MAXSIM_TILED_CASE(2)
@@ -44,13 +48,13 @@ int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t 
   return MAXSIM_ERR_UNSUPPORTED;
 }
 
-template <int DT, bool ARG>
+template <int DT, bool ARG, bool BATCH = false>
 int tiled_by_ksb(int ksb, int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   switch (ksb) {
-  case 1: return tiled_by_qbw<DT, 1, ARG>(qbw, a, di, st);
-  case 2: return tiled_by_qbw<DT, 2, ARG>(qbw, a, di, st);
-  case 4: return tiled_by_qbw<DT, 4, ARG>(qbw, a, di, st);
-  case 8: return tiled_by_qbw<DT, 8, ARG>(qbw, a, di, st);
+  case 1: return tiled_by_qbw<DT, 1, ARG, BATCH>(qbw, a, di, st);
+  case 2: return tiled_by_qbw<DT, 2, ARG, BATCH>(qbw, a, di, st);
+  case 4: return tiled_by_qbw<DT, 4, ARG, BATCH>(qbw, a, di, st);
+  case 8: return tiled_by_qbw<DT, 8, ARG, BATCH>(qbw, a, di, st);
   }
   return MAXSIM_ERR_UNSUPPORTED;
 }
@@ -60,6 +64,8 @@ int tiled_dense_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di, 
 // The same, also writing per-token maxima and argmax; defined in tiled_dense_arg.hip.
 int tiled_dense_argmax_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di,
                            hipStream_t st);
+// Several queries (TiledArgs::n_q) in one pass, dense storage; defined in tiled_batch.hip.
+int tiled_batch_run(const TiledArgs &a, int d, int dtype, const DeviceInfo &di, hipStream_t st);
 // INT8 storage; defined in tiled_i8.hip.
 int tiled_i8_run(const TiledArgs &a, int d, const DeviceInfo &di, hipStream_t st);
 

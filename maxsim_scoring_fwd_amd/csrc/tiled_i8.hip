@@ -6,8 +6,8 @@ namespace maxsim {
 int tiled_i8_run(const TiledArgs &a, int d, const DeviceInfo &di, hipStream_t st) {
   const int ksb = d / 64;
   if (ksb != 1 && ksb != 2 && ksb != 4 && ksb != 8) return MAXSIM_ERR_UNSUPPORTED;
-  if (a.q_len > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
-  const int qbw = tiled_qbw(a.q_len);
+  if (tiled_tokens(a) > tiled_max_q(ksb)) return MAXSIM_ERR_UNSUPPORTED;
+  const int qbw = tiled_qbw(tiled_tokens(a));
   if (a.tok_max) return tiled_by_ksb<DT_I8, true>(ksb, qbw, a, di, st);
   return tiled_by_ksb<DT_I8, false>(ksb, qbw, a, di, st);
 }

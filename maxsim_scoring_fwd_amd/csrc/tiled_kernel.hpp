@@ -23,10 +23,13 @@
 //  * Per tile and query block, the 16x16 accumulator is reduced into a running
 //    max held in one VGPR per lane (plus the argmax when per-token maxima and
 //    argmax are asked for: the lowest row reaching the maximum).
-//  * At the document's end each wave folds its maxima into one partial sum;
-//    the partials meet in LDS and one thread adds them in wave order. These sums
-//    over up to 1024 query tokens are taken in double and rounded once to fp32,
-//    so a score of a few hundred keeps its fp32 precision.
+//  * At the document's end each wave sums its maxima per query; the partial sums
+//    meet in LDS and each query adds them in wave order. These sums over up to
+//    1024 query tokens are taken in double and rounded once to fp32, so a score of
+//    a few hundred keeps its fp32 precision.
+//  * Several queries can share one pass over the documents (each padded to whole
+//    16-token blocks): every document byte then serves n_q queries, and each query
+//    gets its own score per document.
 #pragma once
 
 #include "device_common.hpp"
@@ -59,6 +62,7 @@ struct TiledArgs {
   float *out;
   float *tok_max;           // ARG only: per-token maxima [n_docs][q_len]
   int32_t *tok_arg;         // ARG only: per-token argmax [n_docs][q_len]
+  int n_q = 1;              // queries of q_len tokens each, Q [n_q][q_len][d], out [n_q][n_docs]
 };
 
 __device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int64_t &first,
@@ -79,9 +83,11 @@ __device__ __forceinline__ void tiled_extent(const TiledArgs &a, int64_t b, int6
 
 // DT: storage; KSB: 64-byte chunks per token row (d = KSB * 64 / element bytes);
 // QBW: 16-query blocks per wave (queries per workgroup = 8 * 16 * QBW);
-// ARG: also produce the per-token maxima and argmax; NW: waves per workgroup.
-template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES>
+// ARG: also produce the per-token maxima and argmax (single query); NW: waves per
+// workgroup; BATCH: several queries (TiledArgs::n_q), else exactly one.
+template <int DT, int KSB, int QBW, bool ARG, int NW = TILED_WAVES, bool BATCH = false>
 __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
+  static_assert(!(ARG && BATCH), "per-token outputs come with a single query");
   constexpr int TILED_THREADS = NW * WAVE;
   constexpr int RB = KSB * 64;                         // bytes per token row
   constexpr int PPR = KSB * 4;                         // 16-byte pieces per row
@@ -91,29 +97,44 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   constexpr bool I8 = DT == DT_I8;
   static_assert((PPR & (PPR - 1)) == 0, "swizzle needs a power-of-two row");
   __shared__ __attribute__((aligned(16))) char blk_lds[2][TILED_BLOCK_BYTES];
-  __shared__ double part_lds[NW];
+  __shared__ double part_lds[NW * QBW];  // per (wave, query) segment: its sum of maxima
   __shared__ __attribute__((aligned(16))) float dscale_lds[2][I8 ? BLK_ROWS : 4];
 
   const int lane = threadIdx.x & (WAVE - 1);
   const int r16 = lane & 15, g = lane >> 4;
   const int w = uniform((int)(threadIdx.x >> 6));
   const int q_len = a.q_len;
+  const int q_pad = (q_len + 15) & ~15;  // each query padded to whole 16-token blocks
   const int q_base = w * QBW * 16;
 
   // ---- this wave's query slice, resident as B operands ----
+  // Token t of the workgroup's numbering is token t % q_pad of query t / q_pad; padding
+  // tokens are zero vectors and are left out of the sums.
   u32x4_t qreg[QBW][KSB];
   float qs[QBW];
+  // Row of Q [n_q * q_len] held by the lane's column of query block qb, or -1 (padding).
+  // A 16-token block lies within one padded query, so the query index is wave-uniform.
+  // (A single query: the row is the token index itself.)
+  auto q_row = [&](int qb) -> int {
+    if constexpr (!BATCH) {
+      const int qi = q_base + qb * 16 + r16;
+      return qi < q_len ? qi : -1;
+    }
+    const int tb = uniform(q_base + qb * 16);
+    const int qq = tb / q_pad, pos = tb - qq * q_pad + r16;
+    return qq < a.n_q && pos < q_len ? qq * q_len + pos : -1;
+  };
 #pragma unroll
   for (int qb = 0; qb < QBW; qb++) {
-    const int qi = q_base + qb * 16 + r16;
+    const int row = q_row(qb);
     qs[qb] = 0.f;
     if constexpr (I8) {
-      if (qi < q_len) qs[qb] = a.q_scale[qi];
+      if (row >= 0) qs[qb] = a.q_scale[row];
     }
 #pragma unroll
     for (int c = 0; c < KSB; c++) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (qi < q_len) v = load16(a.Q + (int64_t)qi * RB + c * 64 + g * 16);
+      if (row >= 0) v = load16(a.Q + (int64_t)row * RB + c * 64 + g * 16);
       qreg[qb][c] = v;
     }
   }
@@ -280,7 +301,25 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     }
 
     if (doc_end) {
+      // Each lane adds its maxima over consecutive blocks of one query in double; where the
+      // query changes (wave-uniform) the lanes reduce and the segment's sum goes to LDS slot
+      // w * QBW + (first block of the segment). A query then adds its segments in order.
       double s = 0.0;
+      int seg_q = uniform(q_base / q_pad), seg_k = uniform(w * QBW);
+      // Several queries whose blocks never straddle two waves: each segment is a whole
+      // query, and the wave stores its score directly (no LDS, no barrier).
+      const bool local = BATCH && QBW % (q_pad / 16) == 0;
+      auto flush = [&]() {
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh);
+        if (lane == 0) {
+          if (!local)
+            part_lds[seg_k] = s;
+          else if (seg_q < a.n_q)
+            a.out[(int64_t)seg_q * a.n_docs + b] = empty ? -__builtin_inff() : (float)s;
+        }
+        s = 0.0;
+      };
 #pragma unroll
       for (int qb = 0; qb < QBW; qb++) {
         float v = m[qb];
@@ -299,29 +338,46 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
             v = __builtin_fmaxf(v, ov);
           }
         }
-        const int qi = q_base + qb * 16 + r16;
-        if (qi < q_len) {
-          s += empty ? 0.0 : (double)v;
-          if constexpr (ARG) {
-            if (g == 0) {
-              a.tok_max[b * q_len + qi] = empty ? -__builtin_inff() : v;
-              a.tok_arg[b * q_len + qi] = empty ? -1 : j;
+        if constexpr (!BATCH) {
+          // a single query: token qi
+          const int qi = q_base + qb * 16 + r16;
+          if (qi < q_len) {
+            if (!empty) s += (double)v;
+            if constexpr (ARG) {
+              if (g == 0) {
+                a.tok_max[b * q_len + qi] = empty ? -__builtin_inff() : v;
+                a.tok_arg[b * q_len + qi] = empty ? -1 : j;
+              }
             }
           }
+        } else {
+          const int qq = uniform((q_base + qb * 16) / q_pad);
+          if (qq != seg_q) {
+            flush();
+            seg_q = qq;
+            seg_k = uniform(w * QBW + qb);
+          }
+          if (q_row(qb) >= 0 && !empty) s += (double)v;
         }
         m[qb] = -__builtin_inff();
         arg[qb] = -1;
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      if (lane == 0) part_lds[w] = s;
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        double tot = 0.0;
-        for (int k = 0; k < NW; k++) tot += part_lds[k];
-        a.out[b] = empty ? -__builtin_inff() : (float)tot;
+      flush();
+      if (!local) __syncthreads();  // wave-uniform and the same in every wave
+      if constexpr (!BATCH) {
+        if (threadIdx.x == 0) {  // a single query: one segment per wave
+          double tot = 0.0;
+          for (int k = 0; k < NW; k++) tot += part_lds[k * QBW];
+          a.out[b] = empty ? -__builtin_inff() : (float)tot;
+        }
+      } else if (!local) {
+        const int bpq = q_pad / 16;
+        for (int q = threadIdx.x; q < a.n_q; q += TILED_THREADS) {
+          double tot = 0.0;
+          for (int k = q * bpq; k < (q + 1) * bpq; k++)
+            if (k == q * bpq || k % QBW == 0) tot += part_lds[k];
+          a.out[(int64_t)q * a.n_docs + b] = empty ? -__builtin_inff() : (float)tot;
+        }
       }
     }
     buf ^= 1;

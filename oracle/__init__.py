@@ -217,6 +217,14 @@ def maxsim_argmax(*a, **k):
     return get().maxsim_argmax(*a, **k)
 
 
+def maxsim_batch(Qs, D, dtype: str, offsets=None, nthreads=None) -> np.ndarray:
+    """Several queries Qs [n_q, q_len, d] against the same documents: by definition one
+    single-query oracle score per (query, document); returns float64 [n_q, n_docs]."""
+    if offsets is None:
+        return np.stack([maxsim_fixed(q, D, dtype, nthreads=nthreads) for q in Qs])
+    return np.stack([maxsim_csr(q, D, offsets, dtype, nthreads=nthreads) for q in Qs])
+
+
 def maxsim_backward(*a, **k):
     return get().maxsim_backward(*a, **k)
 

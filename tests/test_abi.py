@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
               "maxsim_score_pq", "maxsim_status_string", "maxsim_version", "maxsim_score_argmax",
-              "maxsim_backward", "maxsim_backward_workspace_size"):
+              "maxsim_backward", "maxsim_backward_workspace_size", "maxsim_score_batch"):
         assert f in names
 
 
@@ -167,6 +167,22 @@ def test_argmax_argument_errors(L):
     assert f(dt=5) == DTYPE
     assert f(tm=P + 2) == ALIGN
     assert f(off=P + 4) == ALIGN
+    assert f(n=0) == OK
+
+
+def test_batch_argument_errors(L):
+    f = lambda **k: L.maxsim_score_batch(k.get("Q", P), k.get("n_q", 4), k.get("q_len", 32),
+                                         k.get("D", P), k.get("off", None), k.get("n", 5),
+                                         k.get("nd", 16), k.get("d", 128), k.get("dt", 0),
+                                         k.get("out", P), None)
+    assert f(n_q=0) == SHAPE
+    assert f(nd=0) == SHAPE
+    assert f(q_len=0) == SHAPE
+    assert f(Q=None) == NULL
+    assert f(out=P + 2) == ALIGN
+    assert f(off=P + 4) == ALIGN
+    assert f(d=768) == UNSUP          # 1536-byte rows: no query-tiled kernel
+    assert f(dt=2, d=256) == UNSUP    # fp32 rows of 1 KiB
     assert f(n=0) == OK
 
 

@@ -1,0 +1,85 @@
+"""GPU parity of several queries scored in one pass over the documents
+(maxsim_score_batch): each (query, document) score against the oracle's single-query score
+of that query (|delta| <= 1e-4), with queries padded inside the kernel, groups of queries
+split across launches, CSR documents with empty ones, and a single query bit-identical to
+the single-query entry point."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from gpu_util import TOL, compare, ms, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ms()
+
+
+def queries(seed, n_q, q_len, d, dtype):
+    Q = gen.tokens(seed, gen.S_QUERY, 0, n_q * q_len, d, dtype)
+    return Q.reshape(n_q, q_len, d)
+
+
+def gpu_batch(Q, D, dtype, offsets=None):
+    import torch
+    off = None if offsets is None else torch.from_numpy(offsets).cuda()
+    out = ms().maxsim_score_batch(gen.to_device(Q, dtype), gen.to_device(D, dtype), off)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+CASES = [  # n_q, q_len, d, dtype, layout
+    (4, 32, 128, "bf16", "fixed"),
+    (32, 32, 128, "bf16", "fixed"),   # 1024 tokens: one launch
+    (40, 32, 128, "bf16", "csr"),     # two launches
+    (3, 7, 64, "fp16", "fixed"),      # padding inside every query
+    (5, 100, 128, "bf16", "csr"),     # 112-token padded queries, 9 per launch
+    (2, 64, 256, "bf16", "fixed"),
+    (6, 33, 128, "fp32", "fixed"),    # fp32 rows of 512 B: 512 tokens per launch
+    (17, 1, 128, "bf16", "csr"),      # one-token queries
+    (3, 1024, 128, "bf16", "fixed"),  # one query per launch
+]
+
+
+@pytest.mark.parametrize("n_q,q_len,d,dtype,layout", CASES)
+def test_batch_matches_single_query_oracle(n_q, q_len, d, dtype, layout):
+    say(f"case: batch n_q={n_q} q_len={q_len} d={d} {dtype} {layout}")
+    seed = 700 + n_q + q_len + d
+    Q = queries(seed, n_q, q_len, d, dtype)
+    if layout == "fixed":
+        c = gen.fixed_corpus(seed, 37, 1, 90, d, dtype)
+        want = oracle.maxsim_batch(Q, c.D, dtype)
+        got = gpu_batch(Q, c.D, dtype)
+    else:
+        lens = np.concatenate([[0, 1, 130, 0, 16, 17], gen.lengths(seed, 40)])
+        c = gen.csr_corpus(seed, len(lens), 1, d, dtype, lens=lens)
+        want = oracle.maxsim_batch(Q, c.D, dtype, offsets=c.offsets)
+        got = gpu_batch(Q, c.D, dtype, c.offsets)
+    assert got.shape == (n_q, want.shape[1])
+    compare(got.ravel(), want.ravel(), what=f"batch n_q={n_q} q_len={q_len}")
+
+
+@pytest.mark.parametrize("q_len", [100, 512])
+def test_single_query_batch_is_bit_identical(q_len):
+    """n_q = 1 runs the same kernel and summation order as maxsim_score_fixed."""
+    import torch
+    say(f"case: batch of one, q_len={q_len}")
+    c = gen.fixed_corpus(720 + q_len, 20, q_len, 150, 128, "bf16")
+    Q, D = gen.to_device(c.Q, "bf16"), gen.to_device(c.D, "bf16")
+    one = ms().maxsim_score_fixed(Q, D)
+    batch = ms().maxsim_score_batch(Q.unsqueeze(0).contiguous(), D)
+    torch.cuda.synchronize()
+    assert torch.equal(one, batch[0])
+
+
+def test_batch_unsupported_row_width_raises():
+    say("case: batch d=768 bf16 (no kernel)")
+    Q = queries(730, 2, 8, 768, "bf16")
+    c = gen.fixed_corpus(730, 3, 1, 16, 768, "bf16")
+    with pytest.raises(Exception):
+        gpu_batch(Q, c.D, "bf16")

@@ -31,7 +31,7 @@ def run(name):
     w = bench.WORKLOADS[name]
     say(f"case: full-size {name} {w}")
     inp = bench.make_inputs(w, torch.device("cuda"))
-    out = torch.empty(w["B"], dtype=torch.float32, device="cuda")
+    out = torch.empty(w.get("n_q", 1) * w["B"], dtype=torch.float32, device="cuda")
     for _, fn in bench.launches(ms(), w, inp, out):
         fn()
     torch.cuda.synchronize()
@@ -191,3 +191,17 @@ def test_train_step_full_size(name):
     mD = oracle.maxsim_backward(absQ, sub & 0x7fff, w["dtype"], ta[ids], np.abs(g[ids]),
                                 offsets=soff)[1]
     check_bound(gD, dD, mD, w["q_len"], w["dtype"], f"{name} dD ({len(ids)} sampled docs)")
+
+
+def test_batch_colbert_q32_sampled():
+    """32 queries against the 100K-document ColBERT corpus in the bench's launch: every
+    query's scores on sampled documents against the oracle."""
+    w, inp, got = run("batch-colbert-q32-b100k")
+    release(inp)
+    got = got.reshape(w["n_q"], w["B"])
+    rng = np.random.default_rng(3)
+    ids = np.unique(np.concatenate([[0, w["B"] - 1], rng.integers(0, w["B"], size=150)]))
+    Q = gen.tokens(w["seed"], gen.S_QUERY, 0, w["n_q"] * w["q_len"], w["d"], w["dtype"])
+    D = gen.fixed_docs_subset(w["seed"], ids, w["nd"], w["d"], w["dtype"])
+    want = oracle.maxsim_batch(Q.reshape(w["n_q"], w["q_len"], w["d"]), D, w["dtype"])
+    compare(got[:, ids].ravel(), want.ravel(), what=f"batch q32 ({len(ids)} sampled docs x 32 queries)")
