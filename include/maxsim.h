@@ -192,6 +192,23 @@ int maxsim_pq_tables(const void *Q, int q_len, int dtype, const float *C, int M,
 int maxsim_score_pq(const float *T, int q_len, int M, int K, const uint8_t *codes,
                     const int64_t *doc_offsets, int64_t n_docs, int nd, float *out, void *stream);
 
+/*
+ * Top-k selection after scoring (the stage that hands the best documents on): for each of
+ * `rows` rows of n scores (a [rows][n] array such as the output of maxsim_score_batch),
+ * the k entries that come first in the order score descending, document index ascending,
+ * in that order. The selection is exact and the same on every run (no atomics).
+ *   scores     fp32 [rows][n]; 1 <= n < 2^31, 1 <= rows <= 65535; NaN is not ordered
+ *   k          1 <= k <= 1024; if k > n the tail holds -inf and index -1
+ *   out_scores fp32 [rows][k]; out_index int32 [rows][k]
+ *   workspace  device buffer of at least maxsim_topk_workspace_size(n, rows, k) bytes,
+ *              8-byte aligned (NULL allowed when that size is 0)
+ */
+int maxsim_topk(const float *scores, int64_t n, int rows, int k, float *out_scores,
+                int32_t *out_index, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes maxsim_topk needs (0 when n fits one 2048-entry chunk or on bad sizes). */
+size_t maxsim_topk_workspace_size(int64_t n, int rows, int k);
+
 /* Static description of a status code. */
 const char *maxsim_status_string(int status);
 

@@ -56,12 +56,15 @@ def lib() -> ctypes.CDLL:
                                       vp, ctypes.c_size_t, vp]
         L.maxsim_backward_workspace_size.argtypes = [i32, i32, i64]
         L.maxsim_backward_workspace_size.restype = ctypes.c_size_t
+        L.maxsim_topk.argtypes = [vp, i64, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.maxsim_topk_workspace_size.argtypes = [i64, i32, i32]
+        L.maxsim_topk_workspace_size.restype = ctypes.c_size_t
         L.maxsim_status_string.argtypes = [i32]
         L.maxsim_status_string.restype = ctypes.c_char_p
         L.maxsim_version.argtypes = []
         for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
                   "maxsim_score_pq", "maxsim_version", "maxsim_score_argmax", "maxsim_backward",
-                  "maxsim_score_batch"):
+                  "maxsim_score_batch", "maxsim_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -196,6 +199,33 @@ def maxsim_score_batch(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tens
                                     _dtype_code(Q), _dev(out, "out"), _stream(stream)),
            "maxsim_score_batch")
     return out
+
+
+def topk_workspace_size(n: int, rows: int, k: int) -> int:
+    """Bytes of workspace maxsim_topk needs."""
+    return int(lib().maxsim_topk_workspace_size(n, rows, k))
+
+
+def maxsim_topk(scores: torch.Tensor, k: int, out_scores=None, out_index=None, workspace=None,
+                stream=None):
+    """The k best entries of each row of scores ([n] or [rows, n] fp32) by (score
+    descending, index ascending). Returns (values, indices) shaped [k] or [rows, k]."""
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    rows, n = (1, scores.shape[0]) if scores.dim() == 1 else scores.shape
+    shape = (k,) if scores.dim() == 1 else (rows, k)
+    if out_scores is None:
+        out_scores = torch.empty(shape, dtype=torch.float32, device=scores.device)
+    if out_index is None:
+        out_index = torch.empty(shape, dtype=torch.int32, device=scores.device)
+    need = topk_workspace_size(n, rows, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().maxsim_topk(_dev(scores, "scores"), n, rows, k, _dev(out_scores, "out_scores"),
+                             _dev(out_index, "out_index"), _dev(workspace, "workspace"), ws_bytes,
+                             _stream(stream)), "maxsim_topk")
+    return out_scores, out_index
 
 
 def backward_workspace_size(q_len: int, d: int, n_docs: int) -> int:

@@ -70,13 +70,6 @@ __device__ __forceinline__ void bwd_extent(const BwdArgs &a, int64_t b, int64_t 
   }
 }
 
-// Order the wave's LDS accesses before and after this point (a wave-level barrier).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // E consecutive elements of storage type DT at p, as fp32 (p aligned to E elements).
 template <int DT, int E>
 __device__ __forceinline__ void load_f32(const char *p, float (&x)[E]) {

@@ -81,6 +81,13 @@ __device__ __forceinline__ u32x4_t load16_nt(const char *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
+// Order the wave's LDS accesses before and after this point (a wave-level barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float max4(f32x4_t v) {
   return __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
 }

@@ -1,0 +1,66 @@
+// libmaxsim top-k entry points (include/maxsim.h): the best k documents of each score row.
+#include <hip/hip_runtime.h>
+
+#include "host_common.hpp"
+#include "topk_kernel.hpp"
+
+using namespace maxsim;
+
+namespace {
+
+int64_t chunks_of(int64_t count) { return (count + TOPK_CHUNK - 1) / TOPK_CHUNK; }
+
+bool topk_args_ok(int64_t n, int rows, int k) {
+  return n >= 1 && n < ((int64_t)1 << 31) && rows >= 1 && rows <= 65535 && k >= 1 &&
+         k <= TOPK_MAX_K;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t maxsim_topk_workspace_size(int64_t n, int rows, int k) {
+  if (!topk_args_ok(n, rows, k)) return 0;
+  const int64_t c1 = chunks_of(n);
+  if (c1 <= 1) return 0;
+  const int64_t c2 = chunks_of(c1 * k);
+  return (size_t)(c1 + (c2 > 1 ? c2 : 0)) * (size_t)k * (size_t)rows * sizeof(uint64_t);
+}
+
+int maxsim_topk(const float *scores, int64_t n, int rows, int k, float *out_scores,
+                int32_t *out_index, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!topk_args_ok(n, rows, k)) return MAXSIM_ERR_SHAPE;
+  if (!scores || !out_scores || !out_index) return MAXSIM_ERR_NULL;
+  if (!aligned(scores, 4) || !aligned(out_scores, 4) || !aligned(out_index, 4) ||
+      (workspace && !aligned(workspace, 8)))
+    return MAXSIM_ERR_ALIGN;
+  const size_t need = maxsim_topk_workspace_size(n, rows, k);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return workspace ? MAXSIM_ERR_SHAPE
+                                                                           : MAXSIM_ERR_NULL;
+  DeviceInfo di;
+  int rc = current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t c1 = chunks_of(n);
+  uint64_t *buf[2] = {(uint64_t *)workspace, (uint64_t *)workspace + (c1 > 1 ? c1 * k * rows : 0)};
+  TopkLevelArgs a{scores, nullptr, n, n, k, nullptr, 0, out_scores, out_index};
+  for (int level = 0;; level++) {
+    const int64_t chunks = chunks_of(a.count);
+    if (chunks == 1) {  // the final chunk: sorted top-k out
+      a.out_keys = nullptr;
+      hipLaunchKernelGGL(topk_level_kernel, dim3(1, (unsigned)rows), dim3(TOPK_THREADS), 0, st, a);
+      return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+    }
+    a.out_keys = buf[level & 1];
+    a.out_stride = chunks * k;
+    hipLaunchKernelGGL(topk_level_kernel, dim3((unsigned)chunks, (unsigned)rows),
+                       dim3(TOPK_THREADS), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
+    a.scores = nullptr;
+    a.in_keys = a.out_keys;
+    a.count = chunks * k;
+    a.in_stride = a.out_stride;
+  }
+}
+
+}  // extern "C"

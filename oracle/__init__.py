@@ -217,6 +217,21 @@ def maxsim_argmax(*a, **k):
     return get().maxsim_argmax(*a, **k)
 
 
+def topk(scores, k: int):
+    """The k best entries of each row of scores by (score descending, index ascending), the
+    ordering used to rank documents (a library sort as the step). Returns (values [rows, k],
+    indices [rows, k]); a row shorter than k is padded with -inf and index -1."""
+    S = np.atleast_2d(np.asarray(scores))
+    rows, n = S.shape
+    vals = np.full((rows, k), -np.inf, dtype=S.dtype)
+    idx = np.full((rows, k), -1, dtype=np.int64)
+    for r in range(rows):
+        order = np.lexsort((np.arange(n), -S[r]))[:k]
+        vals[r, :len(order)] = S[r, order]
+        idx[r, :len(order)] = order
+    return vals, idx
+
+
 def maxsim_batch(Qs, D, dtype: str, offsets=None, nthreads=None) -> np.ndarray:
     """Several queries Qs [n_q, q_len, d] against the same documents: by definition one
     single-query oracle score per (query, document); returns float64 [n_q, n_docs]."""

@@ -477,6 +477,29 @@ def pin_backward_one_token_docs(orc):
     assert np.allclose(dQ, np.broadcast_to(g.astype(np.float64) @ Dd, dQ.shape), rtol=0, atol=1e-12)
 
 
+def pin_topk_brute(orc):
+    """Top-k against repeated extraction of the best remaining entry (largest score, lowest
+    index among equals) on small rows with ties and -inf."""
+    import oracle as oracle_module
+    rng = np.random.default_rng(25)
+    for n, k in ((1, 1), (7, 3), (20, 20), (25, 30), (64, 10)):
+        S = (rng.integers(-4, 5, size=(3, n)) / 4.0).astype(np.float32)
+        S[:, ::5] = -np.inf
+        vals, idx = oracle_module.topk(S, k)
+        for r in range(3):
+            left = list(range(n))
+            for j in range(k):
+                if not left:
+                    assert idx[r, j] == -1 and vals[r, j] == -np.inf
+                    continue
+                best = left[0]
+                for i in left:
+                    if S[r, i] > S[r, best]:
+                        best = i
+                left.remove(best)
+                assert idx[r, j] == best and vals[r, j] == S[r, best], (n, k, r, j)
+
+
 PINS = [
     pin_golden_dense, pin_golden_int8, pin_golden_pq,
     pin_brute_dense, pin_brute_fp16_subnormal, pin_brute_int8, pin_brute_pq,
@@ -484,5 +507,5 @@ PINS = [
     pin_doc_permutation_and_duplicates, pin_padding_and_neighbours, pin_power_of_two_scaling,
     pin_query_permutation, pin_planted_top10,
     pin_argmax_brute, pin_backward_euler, pin_backward_finite_difference,
-    pin_backward_one_token_docs,
+    pin_backward_one_token_docs, pin_topk_brute,
 ]

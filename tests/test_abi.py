@@ -35,7 +35,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
               "maxsim_score_pq", "maxsim_status_string", "maxsim_version", "maxsim_score_argmax",
-              "maxsim_backward", "maxsim_backward_workspace_size", "maxsim_score_batch"):
+              "maxsim_backward", "maxsim_backward_workspace_size", "maxsim_score_batch",
+              "maxsim_topk", "maxsim_topk_workspace_size"):
         assert f in names
 
 
@@ -184,6 +185,22 @@ def test_batch_argument_errors(L):
     assert f(d=768) == UNSUP          # 1536-byte rows: no query-tiled kernel
     assert f(dt=2, d=256) == UNSUP    # fp32 rows of 1 KiB
     assert f(n=0) == OK
+
+
+def test_topk_argument_errors_and_workspace(L):
+    f = lambda **k: L.maxsim_topk(k.get("S", P), k.get("n", 100000), k.get("rows", 1),
+                                  k.get("k", 100), k.get("vo", P), k.get("io", P),
+                                  k.get("ws", P), k.get("wsb", 1 << 30), None)
+    assert f(k=0) == SHAPE and f(k=1025) == SHAPE and f(n=0) == SHAPE and f(rows=0) == SHAPE
+    assert f(S=None) == NULL and f(io=None) == NULL
+    assert f(ws=None) == NULL              # 100000 scores need the workspace
+    assert f(wsb=8) == SHAPE               # too small
+    assert f(S=P + 2) == ALIGN and f(ws=P + 4) == ALIGN
+    w = L.maxsim_topk_workspace_size
+    assert w(2048, 1, 100) == 0            # one chunk: no workspace
+    assert w(100000, 1, 100) == (49 + 3) * 100 * 8  # 49 chunks -> 4900 keys -> 3 chunks -> final
+    assert w(100000, 1, 1024) == (49 + 25) * 1024 * 8
+    assert w(0, 1, 10) == 0 and w(10, 1, 0) == 0
 
 
 def bwd(L, **k):

@@ -205,3 +205,18 @@ def test_batch_colbert_q32_sampled():
     D = gen.fixed_docs_subset(w["seed"], ids, w["nd"], w["d"], w["dtype"])
     want = oracle.maxsim_batch(Q.reshape(w["n_q"], w["q_len"], w["d"]), D, w["dtype"])
     compare(got[:, ids].ravel(), want.ravel(), what=f"batch q32 ({len(ids)} sampled docs x 32 queries)")
+
+
+def test_topk_after_headline_scoring():
+    """Scoring + top-100 at the headline shape in the bench's launch: the selection is exact
+    on the GPU's scores, and agrees with the oracle's ranking of its own scores except at
+    ties within the tolerance."""
+    w, inp, got = run("colbert-topk100-b100k")
+    idx = inp["topk_idx"].cpu().numpy().astype(np.int64)
+    vals = inp["topk_vals"].cpu().numpy()
+    release(inp)
+    g32 = got.astype(np.float32)
+    wv, wi = oracle.topk(g32, 100)
+    assert np.array_equal(idx, wi[0]) and np.array_equal(vals.view(np.uint32), wv[0].view(np.uint32))
+    c = gen.fixed_corpus(w["seed"], w["B"], w["q_len"], w["nd"], w["d"], w["dtype"])
+    topk_agree(got, oracle.maxsim_fixed(c.Q, c.D, w["dtype"]), 100)
