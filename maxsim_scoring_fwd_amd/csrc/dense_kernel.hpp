@@ -332,15 +332,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
           const int qi = qb * 16 + r16;
           if constexpr (ARG) {
             int j = arg[qb];
-#pragma unroll
-            for (int sh = 16; sh <= 32; sh <<= 1) {
-              const float ov = __shfl_xor(v, sh);
-              const int oj = __shfl_xor(j, sh);
-              if (ov > v || (ov == v && oj < j)) {
-                v = ov;
-                j = oj;
-              }
-            }
+            argmax_row_groups(v, j);
             if (g == 0 && qi < q_len) {
               // an empty document's slot multiplied dummy data: report no token
               const int64_t o = slot[p].doc * q_len + qi;
@@ -349,16 +341,12 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
             }
             arg[qb] = -1;
           } else {
-            v = __builtin_fmaxf(v, __shfl_xor(v, 16));
-            v = __builtin_fmaxf(v, __shfl_xor(v, 32));
+            v = max_row_groups(v);
           }
           if (qi < q_len) s += v;
           m[qb] = -__builtin_inff();
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
+        s = sum_row16(s);
         if (slot[p].empty) s = -__builtin_inff();
         if (lane == 0) a.out[slot[p].doc] = s;
       }

@@ -92,4 +92,87 @@ __device__ __forceinline__ float max4(f32x4_t v) {
   return __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
 }
 
+// ---- reductions across lanes, in registers (no LDS round trip) ----
+// A 16x16 accumulator spreads one column over the four 16-lane row groups of the wave
+// (lanes c, c + 16, c + 32, c + 48), and the 16 columns of a row group are its 16 lanes.
+
+// Both members of each pair of row groups, in every lane of the pair: gfx950's
+// v_permlane16_swap exchanges rows 1 and 3 of its first operand with rows 0 and 2 of its
+// second; given the same value twice it returns, in each lane, the lane's own value and
+// the one of lane ^ 16 (in some order). v_permlane32_swap does the same for lane ^ 32.
+template <int XOR> __device__ __forceinline__ void row_pair(uint32_t x, uint32_t &p0, uint32_t &p1) {
+  static_assert(XOR == 16 || XOR == 32, "row groups pair at distance 16 or 32");
+  if constexpr (XOR == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    p0 = p[0];
+    p1 = p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    p0 = p[0];
+    p1 = p[1];
+  }
+}
+
+// Maximum over the four row groups, in every lane.
+__device__ __forceinline__ float max_row_groups(float v) {
+  uint32_t a, b;
+  row_pair<16>(__float_as_uint(v), a, b);
+  v = __builtin_fmaxf(__uint_as_float(a), __uint_as_float(b));
+  row_pair<32>(__float_as_uint(v), a, b);
+  return __builtin_fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+
+// (value, index) with the largest value over the four row groups, equal values keeping
+// the lower index, in every lane. The choice is symmetric in the two members of a pair.
+__device__ __forceinline__ void argmax_row_groups(float &v, int &j) {
+  uint32_t va, vb, ja, jb;
+  row_pair<16>(__float_as_uint(v), va, vb);
+  row_pair<16>((uint32_t)j, ja, jb);
+  bool take_b = __uint_as_float(vb) > __uint_as_float(va) ||
+                (__uint_as_float(vb) == __uint_as_float(va) && (int)jb < (int)ja);
+  v = __uint_as_float(take_b ? vb : va);
+  j = (int)(take_b ? jb : ja);
+  row_pair<32>(__float_as_uint(v), va, vb);
+  row_pair<32>((uint32_t)j, ja, jb);
+  take_b = __uint_as_float(vb) > __uint_as_float(va) ||
+           (__uint_as_float(vb) == __uint_as_float(va) && (int)jb < (int)ja);
+  v = __uint_as_float(take_b ? vb : va);
+  j = (int)(take_b ? jb : ja);
+}
+
+// DPP row permutes (within each 16-lane row): lane ^ 1, lane ^ 2, 7 - lane within each
+// half row, 15 - lane within the row.
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141; // row_half_mirror
+constexpr int DPP_MIRROR = 0x140;      // row_mirror
+
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float x) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the 16 lanes of each row group, in every lane of it. The pairs are those of
+// a butterfly over lane ^ 1, ^ 2, ^ 4, ^ 8 (after the first two steps a quad holds one
+// value, so the mirrors pair whole quads, then whole half rows).
+template <typename T> __device__ __forceinline__ T sum_row16(T s) {
+  if constexpr (sizeof(T) == 8) {
+    s += dpp_f64<DPP_XOR1>(s);
+    s += dpp_f64<DPP_XOR2>(s);
+    s += dpp_f64<DPP_HALF_MIRROR>(s);
+    s += dpp_f64<DPP_MIRROR>(s);
+  } else {
+    s += dpp_f32<DPP_XOR1>(s);
+    s += dpp_f32<DPP_XOR2>(s);
+    s += dpp_f32<DPP_HALF_MIRROR>(s);
+    s += dpp_f32<DPP_MIRROR>(s);
+  }
+  return s;
+}
+
 }  // namespace maxsim

@@ -9,8 +9,18 @@ namespace maxsim {
 // Query tokens of a launch: n_q queries, each padded to whole 16-token blocks.
 inline int tiled_tokens(const TiledArgs &a) { return a.n_q * ((a.q_len + 15) & ~15); }
 
-// Query blocks per wave for a number of query tokens (8 waves x 16 tokens x QBW >= tokens).
-inline int tiled_qbw(int tokens) { return (tokens + TILED_WAVES * 16 - 1) / (TILED_WAVES * 16); }
+// Waves per workgroup. Every wave reads each A operand of a block from LDS and multiplies it
+// by its QBW query blocks, so few blocks per wave leave the kernel bound by LDS reads, and with
+// 8 waves a short query leaves some waves holding only padding. Up to 384 query tokens (dense
+// storage, within the register budget) run 4 waves of ceil(tokens / 64) blocks, two
+// workgroups per CU; longer queries and INT8 run 8 waves.
+inline int tiled_waves(int tokens, int ksb, bool i8) {
+  const int qbw4 = (tokens + 63) / 64;
+  return !i8 && tokens <= 384 && qbw4 * ksb <= 32 ? 4 : TILED_WAVES;
+}
+
+// Query blocks per wave for a number of query tokens (nw waves x 16 tokens x QBW >= tokens).
+inline int tiled_qbw(int tokens, int nw) { return (tokens + nw * 16 - 1) / (nw * 16); }
 
 // Largest query length the tiled kernel holds for KSB 64-byte chunks per row:
 // the slice of one wave needs QBW * KSB * 4 VGPRs, kept at or below 128.
@@ -27,13 +37,13 @@ int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
-template <int DT, int KSB, bool ARG, bool BATCH>
+template <int DT, int KSB, bool ARG, bool BATCH, int NW>
 int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   switch (qbw) {
 #define MAXSIM_TILED_CASE(N)                                                                      \
   case N:                                                                                         \
-    if constexpr (N * KSB <= 32)                                                                  \
-      return launch_tiled<DT, KSB, N, ARG, TILED_WAVES, BATCH>(a, di, st);                        \
+    if constexpr (N * KSB <= 32 && (NW == TILED_WAVES || N <= 6))                                 \
+      return launch_tiled<DT, KSB, N, ARG, NW, BATCH>(a, di, st);                                 \
     break;
     MAXSIM_TILED_CASE(1)
     MAXSIM_TILED_CASE(2)
@@ -48,13 +58,23 @@ int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t 
   return MAXSIM_ERR_UNSUPPORTED;
 }
 
+template <int DT, int KSB, bool ARG, bool BATCH>
+int tiled_by_waves(int tokens, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
+  const int nw = tiled_waves(tokens, KSB, DT == DT_I8);
+  if constexpr (DT != DT_I8) {
+    if (nw == 4) return tiled_by_qbw<DT, KSB, ARG, BATCH, 4>(tiled_qbw(tokens, 4), a, di, st);
+  }
+  return tiled_by_qbw<DT, KSB, ARG, BATCH, TILED_WAVES>(tiled_qbw(tokens, TILED_WAVES), a, di, st);
+}
+
+// Launch for `tokens` query tokens (tiled_tokens) with KSB = ksb.
 template <int DT, bool ARG, bool BATCH = false>
-int tiled_by_ksb(int ksb, int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
+int tiled_by_ksb(int ksb, int tokens, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   switch (ksb) {
-  case 1: return tiled_by_qbw<DT, 1, ARG, BATCH>(qbw, a, di, st);
-  case 2: return tiled_by_qbw<DT, 2, ARG, BATCH>(qbw, a, di, st);
-  case 4: return tiled_by_qbw<DT, 4, ARG, BATCH>(qbw, a, di, st);
-  case 8: return tiled_by_qbw<DT, 8, ARG, BATCH>(qbw, a, di, st);
+  case 1: return tiled_by_waves<DT, 1, ARG, BATCH>(tokens, a, di, st);
+  case 2: return tiled_by_waves<DT, 2, ARG, BATCH>(tokens, a, di, st);
+  case 4: return tiled_by_waves<DT, 4, ARG, BATCH>(tokens, a, di, st);
+  case 8: return tiled_by_waves<DT, 8, ARG, BATCH>(tokens, a, di, st);
   }
   return MAXSIM_ERR_UNSUPPORTED;
 }

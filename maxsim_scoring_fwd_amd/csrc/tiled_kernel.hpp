@@ -9,11 +9,11 @@
 //
 // Flash-MaxSim's forward pass (Figure 1, Algorithm 2) loops over query tiles
 // inside one program per (query, document) pair; on gfx950 the query tiles run
-// concurrently instead: the 8 waves of a workgroup each hold one slice of the
-// query tokens as resident MFMA B operands (QBW blocks of 16 tokens), and one
-// copy of every document block sits in LDS for all of them.
+// concurrently instead: the NW waves of a workgroup (8, or 4 for short queries)
+// each hold one slice of the query tokens as resident MFMA B operands (QBW blocks
+// of 16 tokens), and one copy of every document block sits in LDS for all of them.
 //  * Documents are walked by workgroup (grid stride). A block is 32 KiB of
-//    document tokens: each wave loads 4 KiB of it with 1 KiB contiguous,
+//    document tokens: each wave loads 32 / NW KiB of it with 1 KiB contiguous,
 //    non-temporal loads, writes it to a double-buffered XOR-swizzled LDS tile
 //    and, after one barrier, every wave reads the block's 16-token tiles as
 //    A operands. The next block's loads are in flight while the current one is
@@ -96,6 +96,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   constexpr int LOADS = TILED_BLOCK_BYTES / (TILED_THREADS * 16);  // per lane per block
   constexpr bool I8 = DT == DT_I8;
   static_assert((PPR & (PPR - 1)) == 0, "swizzle needs a power-of-two row");
+  static_assert(!I8 || TILED_THREADS >= BLK_ROWS, "one thread per row stages the INT8 scales");
   __shared__ __attribute__((aligned(16))) char blk_lds[2][TILED_BLOCK_BYTES];
   __shared__ double part_lds[NW * QBW];  // per (wave, query) segment: its sum of maxima
   __shared__ __attribute__((aligned(16))) float dscale_lds[2][I8 ? BLK_ROWS : 4];
@@ -140,22 +141,39 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   }
 
   // ---- block sequence of this workgroup: (doc, block) in order ----
-  int64_t cb = blockIdx.x, cfirst = 0, clen = 0;
-  int cblk = 0;
-  if (cb < a.n_docs) tiled_extent(a, cb, cfirst, clen);
+  // A cursor names block blk of document b (its first token and length); b >= n_docs ends
+  // the sequence.
+  struct Cursor {
+    int64_t b, first, len;
+    int blk;
+  };
+  auto first_block = [&](int64_t b) {
+    Cursor c{b, 0, 0, 0};
+    if (b < a.n_docs) tiled_extent(a, b, c.first, c.len);
+    return c;
+  };
+  auto next_block = [&](const Cursor &c) {
+    const int64_t nblk = c.len == 0 ? 1 : (c.len + BLK_ROWS - 1) / BLK_ROWS;
+    if (c.blk == nblk - 1) return first_block(c.b + gridDim.x);
+    Cursor n = c;
+    n.blk++;
+    return n;
+  };
 
+  // The next block's pieces are loaded into registers while the current one is multiplied.
   u32x4_t pre[LOADS];
   float pre_scale = 0.f;
-  // Issue the loads of block `blk` of the document (first, len); a dummy in-bounds
-  // read of the query when there is nothing to load.
-  auto load_block = [&](bool real, int64_t first, int64_t len, int blk) {
+  // Issue the loads of block c into pre (and its INT8 scales into pre_scale); a dummy
+  // in-bounds read of the query when there is nothing to load.
+  auto load_block = [&](const Cursor &c) {
+    const bool real = c.b < a.n_docs && c.len > 0;
     const char *base = a.Q;
     int last = 0;
     if (real) {
-      const int64_t r0 = (int64_t)blk * BLK_ROWS;
-      const int64_t rem = len - 1 - r0;
+      const int64_t r0 = (int64_t)c.blk * BLK_ROWS;
+      const int64_t rem = c.len - 1 - r0;
       last = rem < BLK_ROWS - 1 ? (int)rem : BLK_ROWS - 1;
-      base = a.D + (first + r0) * RB;
+      base = a.D + (c.first + r0) * RB;
     }
 #pragma unroll
     for (int k = 0; k < LOADS; k++) {
@@ -166,11 +184,14 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     if constexpr (I8) {
       if (threadIdx.x < BLK_ROWS) {
         const int row = (int)threadIdx.x < last ? (int)threadIdx.x : last;
-        pre_scale = real ? a.d_scale[first + (int64_t)blk * BLK_ROWS + row] : 0.f;
+        pre_scale = real ? a.d_scale[c.first + (int64_t)c.blk * BLK_ROWS + row] : 0.f;
       }
     }
   };
-  load_block(cb < a.n_docs && clen > 0, cfirst, clen, 0);
+  Cursor cur = first_block(blockIdx.x);  // the next block to load
+  Cursor meta = cur;                     // the block held by pre
+  load_block(cur);
+  cur = next_block(cur);
 
   float m[QBW];
   int arg[QBW];
@@ -185,7 +206,52 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   constexpr bool PREFETCH = I8 && QBW * KSB <= 16;
   u32x4_t nxt[PREFETCH ? KSB : 1];
 
-  while (cb < a.n_docs) {
+  // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
+  // is a whole query, and the wave stores that query's score itself (no LDS, no barrier).
+  // Its document-end work then leaves the critical path: the scores are stored after the
+  // next block's barrier, so the wait for that block's loads does not include the stores,
+  // and the waves of the second half of the workgroup, which share their SIMDs with the
+  // first half, also take their reductions there, while the other wave of the SIMD
+  // multiplies (with 4 waves, two independent workgroups share each SIMD instead). The
+  // sums and their order are those of the immediate form.
+  const bool local = BATCH && QBW % (q_pad / 16) == 0;
+  const bool defer = local && NW >= TILED_WAVES && w >= NW / 2;
+  bool pend_epi = false, pend_empty = false;  // deferred reductions of document pend_epi_b
+  int64_t pend_epi_b = 0, pend_b = 0;
+  float pend_v = 0.f;  // lane k: the k-th pending score of the wave (document pend_b)
+  int pend_q = -1;     //   and its query, or -1
+  auto local_epilogue = [&](int64_t b, bool empty) {
+    double s = 0.0;
+    int seg_q = uniform(q_base / q_pad), k = 0;
+    auto flush = [&]() {
+      s = sum_row16(s);
+      if (lane == k) {
+        pend_v = empty ? -__builtin_inff() : (float)s;
+        pend_q = seg_q;
+      }
+      k++;
+      s = 0.0;
+    };
+#pragma unroll
+    for (int qb = 0; qb < QBW; qb++) {
+      const float v = max_row_groups(m[qb]);
+      const int qq = uniform((q_base + qb * 16) / q_pad);
+      if (qq != seg_q) {
+        flush();
+        seg_q = qq;
+      }
+      if (q_row(qb) >= 0 && !empty) s += (double)v;
+      m[qb] = -__builtin_inff();
+    }
+    flush();
+    pend_b = b;
+  };
+  auto local_store = [&]() {
+    if (pend_q >= 0 && pend_q < a.n_q) a.out[(int64_t)pend_q * a.n_docs + pend_b] = pend_v;
+    pend_q = -1;
+  };
+
+  while (meta.b < a.n_docs) {
     // this block: stage the prefetched pieces in LDS
     char *tile = blk_lds[buf];
 #pragma unroll
@@ -197,21 +263,25 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     if constexpr (I8) {
       if (threadIdx.x < BLK_ROWS) dscale_lds[buf][threadIdx.x] = pre_scale;
     }
-    const int64_t b = cb, len = clen;
-    const int blk = cblk;
+    const int64_t b = meta.b, len = meta.len;
+    const int blk = meta.blk;
     const bool empty = len == 0;
     const int64_t nblk = empty ? 1 : (len + BLK_ROWS - 1) / BLK_ROWS;
     const bool doc_end = (blk == nblk - 1);
-    // advance and prefetch the next block (of this or the next document)
-    if (doc_end) {
-      cb += gridDim.x;
-      cblk = 0;
-      if (cb < a.n_docs) tiled_extent(a, cb, cfirst, clen);
-    } else {
-      cblk++;
-    }
-    load_block(cb < a.n_docs && clen > 0, cfirst, clen, cblk);
+    // prefetch the next block (of this or the next document)
+    meta = cur;
+    load_block(cur);
+    cur = next_block(cur);
     __syncthreads();
+    if constexpr (BATCH) {
+      if (local) {
+        if (pend_epi) {
+          local_epilogue(pend_epi_b, pend_empty);
+          pend_epi = false;
+        }
+        local_store();
+      }
+    }
 
     // multiply the block's valid tiles against this wave's query slice
     if (!empty) {
@@ -300,24 +370,23 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
       }
     }
 
-    if (doc_end) {
+    if (BATCH && doc_end && local) {
+      if (defer) {
+        pend_epi = true;
+        pend_epi_b = b;
+        pend_empty = empty;
+      } else {
+        local_epilogue(b, empty);
+      }
+    } else if (doc_end) {
       // Each lane adds its maxima over consecutive blocks of one query in double; where the
       // query changes (wave-uniform) the lanes reduce and the segment's sum goes to LDS slot
       // w * QBW + (first block of the segment). A query then adds its segments in order.
       double s = 0.0;
       int seg_q = uniform(q_base / q_pad), seg_k = uniform(w * QBW);
-      // Several queries whose blocks never straddle two waves: each segment is a whole
-      // query, and the wave stores its score directly (no LDS, no barrier).
-      const bool local = BATCH && QBW % (q_pad / 16) == 0;
       auto flush = [&]() {
-#pragma unroll
-        for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh);
-        if (lane == 0) {
-          if (!local)
-            part_lds[seg_k] = s;
-          else if (seg_q < a.n_q)
-            a.out[(int64_t)seg_q * a.n_docs + b] = empty ? -__builtin_inff() : (float)s;
-        }
+        s = sum_row16(s);
+        if (lane == 0) part_lds[seg_k] = s;
         s = 0.0;
       };
 #pragma unroll
@@ -325,18 +394,20 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         float v = m[qb];
         int j = arg[qb];
         // combine the four row groups: larger value wins, equal values keep the lower row
+        if constexpr (ARG) {
+          // through LDS-routed shuffles: the register-pair form needs registers the widest
+          // INT8 instance does not have, and this runs once per document
 #pragma unroll
-        for (int sh = 16; sh <= 32; sh <<= 1) {
-          const float ov = __shfl_xor(v, sh);
-          const int oj = __shfl_xor(j, sh);
-          if (ARG) {
+          for (int sh = 16; sh <= 32; sh <<= 1) {
+            const float ov = __shfl_xor(v, sh);
+            const int oj = __shfl_xor(j, sh);
             if (ov > v || (ov == v && oj < j)) {
               v = ov;
               j = oj;
             }
-          } else {
-            v = __builtin_fmaxf(v, ov);
           }
+        } else {
+          v = max_row_groups(v);
         }
         if constexpr (!BATCH) {
           // a single query: token qi
@@ -363,14 +434,14 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         arg[qb] = -1;
       }
       flush();
-      if (!local) __syncthreads();  // wave-uniform and the same in every wave
+      __syncthreads();  // wave-uniform and the same in every wave
       if constexpr (!BATCH) {
         if (threadIdx.x == 0) {  // a single query: one segment per wave
           double tot = 0.0;
           for (int k = 0; k < NW; k++) tot += part_lds[k * QBW];
           a.out[b] = empty ? -__builtin_inff() : (float)tot;
         }
-      } else if (!local) {
+      } else {
         const int bpq = q_pad / 16;
         for (int q = threadIdx.x; q < a.n_q; q += TILED_THREADS) {
           double tot = 0.0;
@@ -381,6 +452,12 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
       }
     }
     buf ^= 1;
+  }
+  if constexpr (BATCH) {
+    if (local) {
+      if (pend_epi) local_epilogue(pend_epi_b, pend_empty);
+      local_store();
+    }
   }
 }
 
