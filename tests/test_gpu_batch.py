@@ -64,6 +64,24 @@ def test_batch_matches_single_query_oracle(n_q, q_len, d, dtype, layout):
     compare(got.ravel(), want.ravel(), what=f"batch n_q={n_q} q_len={q_len}")
 
 
+def test_batch_more_documents_than_workgroups():
+    """600 CSR documents (empty ones, one-token ones, and ones spanning two 32 KiB blocks)
+    for 32 queries of 32 tokens: every workgroup walks several documents, so the waves that
+    take their document-end reductions after the next block's barrier do so inside the
+    block loop as well as after it."""
+    n_q, q_len, d, dtype = 32, 32, 64, "bf16"
+    say(f"case: batch n_q={n_q} q_len={q_len} d={d} over 600 CSR documents")
+    seed = 741
+    Q = queries(seed, n_q, q_len, d, dtype)
+    lens = gen.lengths(seed, 600, median=20.0, sigma=0.8, lo=1, hi=300)
+    lens[::37] = 0
+    lens[5::53] = 300  # two blocks of 256 rows
+    c = gen.csr_corpus(seed, len(lens), 1, d, dtype, lens=lens)
+    want = oracle.maxsim_batch(Q, c.D, dtype, offsets=c.offsets)
+    got = gpu_batch(Q, c.D, dtype, c.offsets)
+    compare(got.ravel(), want.ravel(), what="batch over 600 documents")
+
+
 @pytest.mark.parametrize("q_len", [100, 512])
 def test_single_query_batch_is_bit_identical(q_len):
     """n_q = 1 runs the same kernel and summation order as maxsim_score_fixed."""

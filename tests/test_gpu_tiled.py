@@ -20,8 +20,10 @@ def _lib():
     ms()
 
 
-LONG = [(q, d) for q in (65, 100, 128, 129, 255, 512, 1000, 1024) for d in (64, 128, 256)
-        if not (d == 256 and q > 512)]
+# Up to 384 query tokens (256 at d=256 bf16) run 4 waves per workgroup, longer ones 8: the
+# lengths include both sides of each switch.
+LONG = [(q, d) for q in (65, 100, 128, 129, 255, 257, 384, 385, 512, 1000, 1024)
+        for d in (64, 128, 256) if not (d == 256 and q > 512)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
