@@ -201,10 +201,9 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     arg[qb] = -1;
   }
   int buf = 0;
-  // INT8 reads the next tile's A operands while the current tile is multiplied and
-  // scaled, where the registers allow it (the query slice takes QBW * KSB * 4 VGPRs)
-  constexpr bool PREFETCH = I8 && QBW * KSB <= 16;
-  u32x4_t nxt[PREFETCH ? KSB : 1];
+  // INT8 where the registers allow it (the query slice takes QBW * KSB * 4 VGPRs): a
+  // two-stage pipeline over the tiles, see the tile loop
+  constexpr bool PIPE = I8 && QBW * KSB <= 16;
 
   // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
   // is a whole query, and the wave stores that query's score itself (no LDS, no barrier).
@@ -293,23 +292,89 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         return *reinterpret_cast<const u32x4_t *>(
             tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
       };
+      // INT8: the int32 dots of tile t, scaled per row, folded into the running max (ties
+      // keep the lowest row)
+      auto scale_fold = [&](int t, const i32x4_t(&acc)[QBW]) {
+        const int row0 = t * 16 + 4 * g;
+        const f32x4_t ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
+#pragma unroll
+        for (int qb = 0; qb < QBW; qb++) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; r++) v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
+          if constexpr (ARG) {
+            // rows past the end duplicate the last token: only a strictly larger
+            // value replaces the maximum, so their index is never taken
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              if (v[r] > m[qb]) {
+                m[qb] = v[r];
+                arg[qb] = blk * BLK_ROWS + row0 + r;
+              }
+            }
+          } else {
+            m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[0]), v[1]);
+            m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[2]), v[3]);
+          }
+        }
+      };
+      if constexpr (PIPE) {
+        // Two accumulator sets: the MFMAs of tile t + 1 are issued before tile t's vector
+        // work (which then needs no result still in the matrix core), and the A operands
+        // of tile t + 2 are read before it too.
+        i32x4_t accA[QBW], accB[QBW];
+        u32x4_t an[KSB];  // A operands of the next tile to multiply
+        // (a read past the last valid tile re-reads it: the steady state has no branches)
+        auto read_next = [&](int t) {
+          const int tt = t < ntiles ? t : ntiles - 1;
+#pragma unroll
+          for (int c = 0; c < KSB; c++) an[c] = read_a(tt, c);
+        };
+        auto mfma_tile = [&](i32x4_t(&acc)[QBW]) {
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) acc[qb] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < KSB; c++)
+#pragma unroll
+            for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(an[c], qreg[qb][c], acc[qb]);
+        };
+        // one MFMA, then a share of the vector work, in turn: a wave keeps the matrix core
+        // and the vector unit busy at once
+        auto interleave = [&]() {
+          constexpr int VPM = (14 + KSB - 1) / KSB;  // VALU per MFMA (~14 per query block)
+          __builtin_amdgcn_sched_group_barrier(0x100, KSB, 0);  // the A reads first
+#pragma unroll
+          for (int i = 0; i < QBW * KSB; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
+        };
+        read_next(0);
+        mfma_tile(accA);
+        read_next(1);
+        int t = 0;
+        for (; t + 2 < ntiles; t += 2) {  // fold tiles t, t + 1; multiply t + 1, t + 2
+          mfma_tile(accB);
+          read_next(t + 2);
+          scale_fold(t, accA);
+          interleave();
+          mfma_tile(accA);
+          read_next(t + 3);
+          scale_fold(t + 1, accB);
+          interleave();
+        }
+        if (t + 1 < ntiles) {  // two tiles left: t in accA, t + 1 in an
+          mfma_tile(accB);
+          scale_fold(t, accA);
+          scale_fold(t + 1, accB);
+        } else {
+          scale_fold(t, accA);
+        }
+      } else {
       for (int t = 0; t < ntiles; t++) {
         u32x4_t aop[KSB];
-        if constexpr (PREFETCH) {
-          if (t == 0) {
 #pragma unroll
-            for (int c = 0; c < KSB; c++) nxt[c] = read_a(0, c);
-          }
-#pragma unroll
-          for (int c = 0; c < KSB; c++) aop[c] = nxt[c];
-          if (t + 1 < ntiles) {
-#pragma unroll
-            for (int c = 0; c < KSB; c++) nxt[c] = read_a(t + 1, c);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
-        }
+        for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
         // all query blocks' accumulators are live: consecutive MFMAs are independent
         if constexpr (I8) {
           i32x4_t acc[QBW];
@@ -319,29 +384,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
           for (int c = 0; c < KSB; c++)
 #pragma unroll
             for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(aop[c], qreg[qb][c], acc[qb]);
-          // scaled similarity per row, then the running max (ties keep the lowest row)
-          const int row0 = t * 16 + 4 * g;
-          const f32x4_t ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
-#pragma unroll
-          for (int qb = 0; qb < QBW; qb++) {
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
-            if constexpr (ARG) {
-              // rows past the end duplicate the last token: only a strictly larger
-              // value replaces the maximum, so their index is never taken
-#pragma unroll
-              for (int r = 0; r < 4; r++) {
-                if (v[r] > m[qb]) {
-                  m[qb] = v[r];
-                  arg[qb] = blk * BLK_ROWS + row0 + r;
-                }
-              }
-            } else {
-              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[0]), v[1]);
-              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[2]), v[3]);
-            }
-          }
+          scale_fold(t, acc);
         } else {
           f32x4_t acc[QBW];
 #pragma unroll
@@ -367,6 +410,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
             for (int qb = 0; qb < QBW; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
           }
         }
+      }
       }
     }
 
