@@ -49,6 +49,9 @@ __device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c
                                                __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
 }
 
+template <bool INT> struct AccType { using type = f32x4_t; };
+template <> struct AccType<true> { using type = i32x4_t; };
+
 struct TiledArgs {
   const char *Q;
   int q_len;
@@ -201,9 +204,11 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     arg[qb] = -1;
   }
   int buf = 0;
-  // INT8 where the registers allow it (the query slice takes QBW * KSB * 4 VGPRs): a
-  // two-stage pipeline over the tiles, see the tile loop
+  // A two-stage pipeline over the tiles (see the tile loop) for INT8, whose vector work per
+  // tile outweighs its MFMAs, where the registers allow a second accumulator set (the query
+  // slice takes QBW * KSB * 4 VGPRs, each accumulator set QBW * 4).
   constexpr bool PIPE = I8 && QBW * KSB <= 16;
+  using AccT = typename AccType<I8>::type;
 
   // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
   // is a whole query, and the wave stores that query's score itself (no LDS, no barrier).
@@ -292,19 +297,39 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         return *reinterpret_cast<const u32x4_t *>(
             tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
       };
-      // INT8: the int32 dots of tile t, scaled per row, folded into the running max (ties
-      // keep the lowest row)
-      auto scale_fold = [&](int t, const i32x4_t(&acc)[QBW]) {
+      // all query blocks' accumulators are live: consecutive MFMAs are independent
+      auto mfma_tile = [&](AccT(&acc)[QBW], const u32x4_t(&aop)[KSB]) {
+#pragma unroll
+        for (int qb = 0; qb < QBW; qb++) acc[qb] = AccT{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < KSB; c++)
+#pragma unroll
+          for (int qb = 0; qb < QBW; qb++) {
+            if constexpr (I8)
+              acc[qb] = chunk_mfma_i8(aop[c], qreg[qb][c], acc[qb]);
+            else
+              acc[qb] = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc[qb]);
+          }
+      };
+      // tile t's similarities (INT8: the int32 dots scaled per row) folded into the running
+      // max; with the argmax, ties keep the lowest row (the lane holds rows 4g .. 4g + 3 of
+      // the tile in increasing order, and rows past the end duplicate the last token, so
+      // only a strictly larger value replaces the maximum and their index is never taken)
+      auto fold = [&](int t, const AccT(&acc)[QBW]) {
         const int row0 = t * 16 + 4 * g;
-        const f32x4_t ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
+        f32x4_t ds;
+        if constexpr (I8) ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
 #pragma unroll
         for (int qb = 0; qb < QBW; qb++) {
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; r++) v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
+          for (int r = 0; r < 4; r++) {
+            if constexpr (I8)
+              v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
+            else
+              v[r] = acc[qb][r];
+          }
           if constexpr (ARG) {
-            // rows past the end duplicate the last token: only a strictly larger
-            // value replaces the maximum, so their index is never taken
 #pragma unroll
             for (int r = 0; r < 4; r++) {
               if (v[r] > m[qb]) {
@@ -312,9 +337,11 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
                 arg[qb] = blk * BLK_ROWS + row0 + r;
               }
             }
-          } else {
+          } else if constexpr (I8) {
             m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[0]), v[1]);
             m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[2]), v[3]);
+          } else {
+            m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
           }
         }
       };
@@ -322,7 +349,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         // Two accumulator sets: the MFMAs of tile t + 1 are issued before tile t's vector
         // work (which then needs no result still in the matrix core), and the A operands
         // of tile t + 2 are read before it too.
-        i32x4_t accA[QBW], accB[QBW];
+        AccT accA[QBW], accB[QBW];
         u32x4_t an[KSB];  // A operands of the next tile to multiply
         // (a read past the last valid tile re-reads it: the steady state has no branches)
         auto read_next = [&](int t) {
@@ -330,18 +357,12 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
 #pragma unroll
           for (int c = 0; c < KSB; c++) an[c] = read_a(tt, c);
         };
-        auto mfma_tile = [&](i32x4_t(&acc)[QBW]) {
-#pragma unroll
-          for (int qb = 0; qb < QBW; qb++) acc[qb] = i32x4_t{0, 0, 0, 0};
-#pragma unroll
-          for (int c = 0; c < KSB; c++)
-#pragma unroll
-            for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(an[c], qreg[qb][c], acc[qb]);
-        };
         // one MFMA, then a share of the vector work, in turn: a wave keeps the matrix core
         // and the vector unit busy at once
         auto interleave = [&]() {
-          constexpr int VPM = (14 + KSB - 1) / KSB;  // VALU per MFMA (~14 per query block)
+          // vector instructions per query block: ~14 (per row a convert, two products,
+          // and half a three-way max)
+          constexpr int VPM = (14 + KSB - 1) / KSB;
           __builtin_amdgcn_sched_group_barrier(0x100, KSB, 0);  // the A reads first
 #pragma unroll
           for (int i = 0; i < QBW * KSB; i++) {
@@ -350,67 +371,35 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
           }
         };
         read_next(0);
-        mfma_tile(accA);
+        mfma_tile(accA, an);
         read_next(1);
         int t = 0;
         for (; t + 2 < ntiles; t += 2) {  // fold tiles t, t + 1; multiply t + 1, t + 2
-          mfma_tile(accB);
+          mfma_tile(accB, an);
           read_next(t + 2);
-          scale_fold(t, accA);
+          fold(t, accA);
           interleave();
-          mfma_tile(accA);
+          mfma_tile(accA, an);
           read_next(t + 3);
-          scale_fold(t + 1, accB);
+          fold(t + 1, accB);
           interleave();
         }
         if (t + 1 < ntiles) {  // two tiles left: t in accA, t + 1 in an
-          mfma_tile(accB);
-          scale_fold(t, accA);
-          scale_fold(t + 1, accB);
+          mfma_tile(accB, an);
+          fold(t, accA);
+          fold(t + 1, accB);
         } else {
-          scale_fold(t, accA);
+          fold(t, accA);
         }
       } else {
-      for (int t = 0; t < ntiles; t++) {
-        u32x4_t aop[KSB];
+        for (int t = 0; t < ntiles; t++) {
+          u32x4_t aop[KSB];
 #pragma unroll
-        for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
-        // all query blocks' accumulators are live: consecutive MFMAs are independent
-        if constexpr (I8) {
-          i32x4_t acc[QBW];
-#pragma unroll
-          for (int qb = 0; qb < QBW; qb++) acc[qb] = i32x4_t{0, 0, 0, 0};
-#pragma unroll
-          for (int c = 0; c < KSB; c++)
-#pragma unroll
-            for (int qb = 0; qb < QBW; qb++) acc[qb] = chunk_mfma_i8(aop[c], qreg[qb][c], acc[qb]);
-          scale_fold(t, acc);
-        } else {
-          f32x4_t acc[QBW];
-#pragma unroll
-          for (int qb = 0; qb < QBW; qb++) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < KSB; c++)
-#pragma unroll
-            for (int qb = 0; qb < QBW; qb++)
-              acc[qb] = ChunkMfma<DT>::run(aop[c], qreg[qb][c], acc[qb]);
-          if constexpr (ARG) {
-            // lane holds rows 4g .. 4g + 3 of the tile, in increasing order
-            const int row0 = blk * BLK_ROWS + t * 16 + 4 * g;
-#pragma unroll
-            for (int qb = 0; qb < QBW; qb++)
-#pragma unroll
-              for (int r = 0; r < 4; r++)
-                if (acc[qb][r] > m[qb]) {
-                  m[qb] = acc[qb][r];
-                  arg[qb] = row0 + r;
-                }
-          } else {
-#pragma unroll
-            for (int qb = 0; qb < QBW; qb++) m[qb] = __builtin_fmaxf(m[qb], max4(acc[qb]));
-          }
+          for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
+          AccT acc[QBW];
+          mfma_tile(acc, aop);
+          fold(t, acc);
         }
-      }
       }
     }
 
