@@ -204,10 +204,11 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     arg[qb] = -1;
   }
   int buf = 0;
-  // A two-stage pipeline over the tiles (see the tile loop) for INT8, whose vector work per
-  // tile outweighs its MFMAs, where the registers allow a second accumulator set (the query
-  // slice takes QBW * KSB * 4 VGPRs, each accumulator set QBW * 4).
-  constexpr bool PIPE = I8 && QBW * KSB <= 16;
+  // A two-stage pipeline over the tiles (see the tile loop) where the registers allow a
+  // second accumulator set (the query slice takes QBW * KSB * 4 VGPRs, each accumulator set
+  // QBW * 4): INT8, whose vector work per tile outweighs its MFMAs, and the 4-wave dense
+  // instances (short queries, two workgroups per CU), whose slices are small.
+  constexpr bool PIPE = QBW * KSB <= 16 && (I8 || NW == 4);
   using AccT = typename AccType<I8>::type;
 
   // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
@@ -360,9 +361,11 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         // one MFMA, then a share of the vector work, in turn: a wave keeps the matrix core
         // and the vector unit busy at once
         auto interleave = [&]() {
-          // vector instructions per query block: ~14 (per row a convert, two products,
-          // and half a three-way max)
-          constexpr int VPM = (14 + KSB - 1) / KSB;
+          // vector instructions per query block: INT8 ~14 (per row a convert, two products,
+          // and half a three-way max), the argmax ~12 (a compare and two selects per row),
+          // a plain max ~4
+          constexpr int VQB = I8 ? 14 : (ARG ? 12 : 4);
+          constexpr int VPM = (VQB + KSB - 1) / KSB;
           __builtin_amdgcn_sched_group_barrier(0x100, KSB, 0);  // the A reads first
 #pragma unroll
           for (int i = 0; i < QBW * KSB; i++) {
