@@ -209,6 +209,10 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   // QBW * 4): INT8, whose vector work per tile outweighs its MFMAs, and the 4-wave dense
   // instances (short queries, two workgroups per CU), whose slices are small.
   constexpr bool PIPE = QBW * KSB <= 16 && (I8 || NW == 4);
+  // The 8-wave dense instances of the several-query pass pipeline by halves of the query
+  // slice (no extra registers). Measured: 32 ColBERT queries +6%; the single long query
+  // (ColPali shape, the same loop) -3%, so it keeps the plain loop.
+  constexpr bool HALF = BATCH && !PIPE && !I8 && NW >= TILED_WAVES && QBW % 2 == 0;
   using AccT = typename AccType<I8>::type;
 
   // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
@@ -394,6 +398,66 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         } else {
           fold(t, accA);
         }
+      } else if constexpr (HALF) {
+        // No registers for a second accumulator set: the query blocks of a tile are taken in
+        // two halves, and each half's MFMAs are interleaved with the folding of the other
+        // half, whose results were issued half a tile earlier. The next tile's A operands
+        // are read as soon as the current tile's last MFMA has taken them.
+        constexpr int H = QBW / 2;
+        AccT accA[H], accB[H];  // query blocks 0 .. H-1 and H .. QBW-1
+        u32x4_t aop[KSB];
+        auto mfma_half = [&](AccT(&acc)[H], int q0) {
+#pragma unroll
+          for (int i = 0; i < H; i++) acc[i] = AccT{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < KSB; c++)
+#pragma unroll
+            for (int i = 0; i < H; i++) acc[i] = ChunkMfma<DT>::run(aop[c], qreg[q0 + i][c], acc[i]);
+        };
+        auto fold_half = [&](int t, const AccT(&acc)[H], int q0) {
+          const int row0 = blk * BLK_ROWS + t * 16 + 4 * g;
+#pragma unroll
+          for (int i = 0; i < H; i++) {
+            if constexpr (ARG) {
+#pragma unroll
+              for (int r = 0; r < 4; r++) {
+                if (acc[i][r] > m[q0 + i]) {
+                  m[q0 + i] = acc[i][r];
+                  arg[q0 + i] = row0 + r;
+                }
+              }
+            } else {
+              m[q0 + i] = __builtin_fmaxf(m[q0 + i], max4(acc[i]));
+            }
+          }
+        };
+        auto interleave_half = [&]() {
+          constexpr int VPM = ((ARG ? 12 : 4) + KSB - 1) / KSB;
+#pragma unroll
+          for (int i = 0; i < H * KSB; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
+        };
+        auto read_tile = [&](int t) {
+#pragma unroll
+          for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
+        };
+        read_tile(0);
+        mfma_half(accA, 0);
+        int t = 0;
+        for (; t + 1 < ntiles; t++) {
+          mfma_half(accB, H);
+          fold_half(t, accA, 0);
+          interleave_half();
+          read_tile(t + 1);
+          mfma_half(accA, 0);
+          fold_half(t, accB, H);
+          interleave_half();
+        }
+        mfma_half(accB, H);
+        fold_half(t, accA, 0);
+        fold_half(t, accB, H);
       } else {
         for (int t = 0; t < ntiles; t++) {
           u32x4_t aop[KSB];
