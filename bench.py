@@ -82,7 +82,21 @@ KERNEL_SOURCES = {
               "dense_dispatch.hpp", "dense_bf16.hip"],
     "train": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "backward_kernel.hpp",
               "backward.hip"],
+    "tiled": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "tiled_kernel.hpp",
+              "tiled_dispatch.hpp", "tiled_dense.hip", "tiled_i8.hip", "tiled_batch.hip"],
+    "pq": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "pq_kernel.hpp"],
 }
+
+
+def kernel_family(w) -> str:
+    """Which kernel sources a workload's scoring runs: the one-wave-per-document dense
+    kernel (up to 64 query tokens), the query-tiled kernel (longer queries, INT8, several
+    queries per pass), the PQ kernels, or the training step's backward."""
+    if w["path"] in ("train", "pq"):
+        return w["path"]
+    if w["path"] in ("i8", "batch") or w["q_len"] > 64:
+        return "tiled"
+    return "dense"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PQ_M, PQ_K, PQ_DSUB = 16, 256, 8
 
@@ -500,14 +514,14 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
-        if rec and rec.get("kernel_hash") == kernel_hash(w["path"]):
+        if rec and rec.get("kernel_hash") == kernel_hash(kernel_family(w)):
             traffic = rec.get("bytes_per_launch")
 
     context = {"dominant_kernel": steps_fns[di][0], "kernel_ms_avg": round(avg_dom, 5),
                "kernel_ms_min": round(min(dom_ms), 5), "work_per_launch": work,
                "hbm_bytes_per_step": footprint,
                "hbm_GBps": round(footprint / (avg_step * 1e-3) / 1e9, 1),
-               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash(w["path"])}
+               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash(kernel_family(w))}
     if w.get("pool") and w["pool"] < w["B"]:
         context["pool"] = f"{w['pool']} distinct documents repeated to {w['B']}"
     if not args.no_calib:
