@@ -8,7 +8,8 @@
 //  * One wave owns one document at a time (Flash-MaxSim Figure 1: one program
 //    per (query, document) pair); there is no cross-wave communication. The
 //    grid is persistent, sized to fill every CU. Fixed-length documents are
-//    walked with a stride of the number of waves. CSR documents of varying
+//    walked with a stride of the number of waves, or, with at least four
+//    documents per wave, as one contiguous range per wave. CSR documents of varying
 //    length are split into contiguous, token-balanced document ranges: each
 //    wave finds its range with a 64-way parallel search over the offsets, so
 //    no wave is left with a long tail of work.
@@ -62,6 +63,7 @@ struct DenseArgs {
   float *out;
   float *tok_max;          // ARG only: per-token maxima [n_docs][q_len]
   int32_t *tok_arg;        // ARG only: per-token argmax [n_docs][q_len]
+  int contiguous = 0;      // fixed layout: wave w takes documents [B*w/W, B*(w+1)/W)
 };
 
 constexpr int DENSE_THREADS = 256;
@@ -193,6 +195,10 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
     pb = uniform(wave_lower_bound(a.offsets, a.n_docs + 1, lo, lane));
     pend = wave == nwaves - 1 ? a.n_docs : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, hi, lane));
     if (wave == 0) pb = 0;
+    pstep = 1;
+  } else if (a.contiguous) {
+    pb = a.n_docs * wave / nwaves;
+    pend = a.n_docs * (wave + 1) / nwaves;
     pstep = 1;
   }
   int64_t pfirst = 0, plen = 0, ptile = 0;

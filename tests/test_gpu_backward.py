@@ -97,6 +97,29 @@ def check_argmax(c, what):
     say(f"  {what}: argmax equal on {unique} unique (doc, token) pairs, {forced} near-ties valid")
 
 
+def test_argmax_many_documents_per_wave():
+    """The forward with argmax where every wave scores a contiguous range of at least 4
+    fixed-length documents (40000 documents of 11 tokens, d=64): scores bit-identical to the
+    plain forward, maxima within the margin, argmax as in check_argmax (vectorised)."""
+    say("case: argmax, 40000 docs, Nd=11, d=64 bf16")
+    c = gen.fixed_corpus(4200, 40000, 32, 11, 64, "bf16")
+    s, tm, ta, plain = gpu_argmax(c)
+    assert np.array_equal(s.view(np.uint32), plain.view(np.uint32)), "scores differ"
+    ws, wtm, wta = oracle.maxsim_argmax(c.Q, c.D, "bf16")
+    qd, Dd = dec(c.Q, "bf16"), dec(c.D, "bf16")
+    S = (Dd.reshape(-1, Dd.shape[-1]) @ qd.T).reshape(Dd.shape[0], Dd.shape[1], -1)
+    S = S.transpose(0, 2, 1)  # [doc, query token, doc token]
+    mg = margin_for(64)
+    assert np.all(np.abs(tm - wtm) <= mg), np.abs(tm - wtm).max()
+    srt = np.sort(S, axis=2)
+    unique = srt[:, :, -1] - srt[:, :, -2] > 2 * mg
+    assert np.array_equal(ta[unique], wta[unique])
+    assert np.all((ta >= 0) & (ta < 11))
+    chosen = np.take_along_axis(S, ta[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+    assert np.all(chosen[~unique] >= wtm[~unique] - mg)
+    say(f"  argmax equal on {int(unique.sum())} unique pairs, {int((~unique).sum())} near-ties valid")
+
+
 DENSE_Q = [1, 16, 32, 33, 64]
 
 
