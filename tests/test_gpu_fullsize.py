@@ -193,10 +193,11 @@ def test_train_step_full_size(name):
     check_bound(gD, dD, mD, w["q_len"], w["dtype"], f"{name} dD ({len(ids)} sampled docs)")
 
 
-def test_batch_colbert_q32_sampled():
-    """32 queries against the 100K-document ColBERT corpus in the bench's launch: every
+@pytest.mark.parametrize("name", ["batch-colbert-q32-b100k", "batch-colbert-q8-b100k"])
+def test_batch_colbert_sampled(name):
+    """32 (8) queries against the 100K-document ColBERT corpus in the bench's launch: every
     query's scores on sampled documents against the oracle."""
-    w, inp, got = run("batch-colbert-q32-b100k")
+    w, inp, got = run(name)
     release(inp)
     got = got.reshape(w["n_q"], w["B"])
     rng = np.random.default_rng(3)
@@ -204,7 +205,90 @@ def test_batch_colbert_q32_sampled():
     Q = gen.tokens(w["seed"], gen.S_QUERY, 0, w["n_q"] * w["q_len"], w["d"], w["dtype"])
     D = gen.fixed_docs_subset(w["seed"], ids, w["nd"], w["d"], w["dtype"])
     want = oracle.maxsim_batch(Q.reshape(w["n_q"], w["q_len"], w["d"]), D, w["dtype"])
-    compare(got[:, ids].ravel(), want.ravel(), what=f"batch q32 ({len(ids)} sampled docs x 32 queries)")
+    compare(got[:, ids].ravel(), want.ravel(),
+            what=f"{name} ({len(ids)} sampled docs x {w['n_q']} queries)")
+
+
+def test_batch_q32_topk100():
+    """32 queries, then the top-100 of each query's row, in the bench's launch: the selection
+    is exact on the GPU's scores (values bit for bit, indices equal) for every query."""
+    w, inp, got = run("batch-colbert-q32-topk100-b100k")
+    idx = inp["topk_idx"].cpu().numpy().astype(np.int64)
+    vals = inp["topk_vals"].cpu().numpy()
+    release(inp)
+    g32 = got.astype(np.float32).reshape(w["n_q"], w["B"])
+    wv, wi = oracle.topk(g32, 100)
+    assert np.array_equal(idx.reshape(wi.shape), wi)
+    assert np.array_equal(vals.reshape(wv.shape).view(np.uint32), wv.view(np.uint32))
+
+
+def test_train_colpali_full_size():
+    """The training step at the ColPali shape (Lq = Ld = 1024, d = 128, 10K documents from a
+    pool of 2048) in the bench's launch. Forward: scores, per-token maxima and argmax of
+    sampled documents against the oracle, and every replica equal to its pool document.
+    Backward (from the step's own argmax, at full size): Euler's identity for a function
+    positively homogeneous of degree one, <dQ, Q> = <dD, D> = sum_b g_b score_b, within
+    the rounding of the bf16 gradients (2^-8 sum |dQ| |Q|) plus the score tolerance."""
+    import torch
+
+    from oracle_pins import dec
+    w, inp, got = run("train-colpali-b10k")
+    pool, B = w["pool"], w["B"]
+    ta_gpu = inp["tok_arg"].cpu().numpy()
+    tm_gpu = inp["tok_max"].cpu().numpy().astype(np.float64)
+    b = np.arange(B)
+    assert np.array_equal(got, got[b % pool]) and np.array_equal(ta_gpu, ta_gpu[b % pool])
+    g = inp["grad"].cpu().numpy().astype(np.float64)
+
+    def dot64(x, y):
+        s = 0.0
+        for r0 in range(0, x.shape[0], 1 << 20):
+            s += float((x[r0:r0 + (1 << 20)].double() * y[r0:r0 + (1 << 20)].double()).sum())
+        return s
+
+    def absdot64(x, y):
+        s = 0.0
+        for r0 in range(0, x.shape[0], 1 << 20):
+            s += float((x[r0:r0 + (1 << 20)].double().abs() *
+                        y[r0:r0 + (1 << 20)].double().abs()).sum())
+        return s
+
+    Qt, Dt = inp["Q"], inp["D"]
+    Df = Dt.reshape(B * w["nd"], w["d"])
+    target = float(np.dot(g, got))
+    tol = float(np.abs(g).sum()) * TOL
+
+    def euler(dQ, dD, rel, what):
+        dD = dD.reshape(B * w["nd"], w["d"])
+        eq, eqb = dot64(dQ, Qt), rel * absdot64(dQ, Qt) + tol
+        ed, edb = dot64(dD, Df), rel * absdot64(dD, Df) + tol
+        say(f"  {what}: sum g score {target:.3f}; <dQ,Q> off by {abs(eq - target):.3e} "
+            f"(bound {eqb:.3e}), <dD,D> off by {abs(ed - target):.3e} (bound {edb:.3e})")
+        assert abs(eq - target) <= eqb and abs(ed - target) <= edb, what
+
+    # the step's bf16 gradients: one rounding to bf16 (2^-8) per element dominates
+    euler(inp["dQ"], inp["dD"], 2.0 ** -8, "bf16 gradients")
+    # the same backward with fp32 gradients: dD rows sum at most q_len query rows and scale
+    # by g once, dQ sums fp32 partials of a few documents per range in double:
+    # gamma_{q_len + 2} covers both
+    dQ32, dD32 = ms().maxsim_backward(Qt, Dt, inp["tok_arg"], inp["grad"], None,
+                                      grad_dtype=torch.float32, workspace=inp["workspace"])
+    torch.cuda.synchronize()
+    n = w["q_len"] + 2
+    euler(dQ32, dD32, n * 2.0 ** -24 / (1 - n * 2.0 ** -24), "fp32 gradients")
+    del dQ32, dD32
+    release(inp)
+
+    ids = np.array([0, 1, pool - 1])
+    Q = gen.tokens(w["seed"], gen.S_QUERY, 0, w["q_len"], w["d"], w["dtype"])
+    D = gen.fixed_docs_subset(w["seed"], ids, w["nd"], w["d"], w["dtype"])
+    ws, tm, ta = oracle.maxsim_argmax(Q, D, w["dtype"])
+    compare(got[ids], ws, what="train-colpali scores (sampled docs)")
+    assert np.abs(tm_gpu[ids] - tm).max() <= 2e-5
+    Qd = dec(Q, w["dtype"])
+    nd = _argmax_rule(Qd, lambda k: dec(D[k], w["dtype"]), np.arange(len(ids)), ta_gpu[ids], ta,
+                      tm, 2e-5)
+    say(f"  train-colpali: argmax differs from the oracle's on {nd} near-tied pairs")
 
 
 def test_topk_after_headline_scoring():
