@@ -32,7 +32,7 @@ constexpr int PQ_M = 16;
 constexpr int PQ_K = 256;
 constexpr int PQ_QS = 8;        // query tokens per LDS slice
 constexpr int PQ_THREADS = 1024;
-constexpr int PQ_CHUNK = 64;    // documents per chunk
+constexpr int PQ_CHUNK = 64;    // largest number of documents per chunk (LDS arrays)
 constexpr int PQ_PAIRS = PQ_THREADS / 2;  // token lanes per workgroup (two threads each)
 
 struct PqTableArgs {
@@ -52,6 +52,7 @@ struct PqScoreArgs {
   int64_t n_docs;
   int nd;
   float *out;
+  int chunk_docs = PQ_CHUNK;  // documents per chunk, 1 .. PQ_CHUNK
 };
 
 template <int DT> __device__ __forceinline__ float decode_elem(const char *Q, int64_t idx);
@@ -91,11 +92,12 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
   const int h = tid & 1;                        // which 4 of the slice's 8 query tokens
   const int q_len = a.q_len;
   const int nslices = (q_len + PQ_QS - 1) / PQ_QS;
-  const int64_t nchunks = (a.n_docs + PQ_CHUNK - 1) / PQ_CHUNK;
+  const int cd = a.chunk_docs;
+  const int64_t nchunks = (a.n_docs + cd - 1) / cd;
 
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
-    const int64_t d0 = ch * PQ_CHUNK;
-    const int ndc = (int)(a.n_docs - d0 < PQ_CHUNK ? a.n_docs - d0 : PQ_CHUNK);
+    const int64_t d0 = ch * cd;
+    const int ndc = (int)(a.n_docs - d0 < cd ? a.n_docs - d0 : cd);
     int64_t tok0;
     __syncthreads();  // the previous chunk is done with coff and part
     if (a.offsets) {
@@ -195,12 +197,23 @@ inline int pq_tables_run(const PqTableArgs &a, const DeviceInfo &, hipStream_t s
 }
 
 inline int pq_score_run(const PqScoreArgs &a, const DeviceInfo &di, hipStream_t st) {
-  const int64_t nchunks = (a.n_docs + PQ_CHUNK - 1) / PQ_CHUNK;
   const int bpc = blocks_per_cu((const void *)pq_score_kernel, PQ_THREADS, 0);
   const int64_t max_wg = (int64_t)bpc * di.cus;
+  // Chunks fill whole rounds of the resident workgroups: with R the rounds that chunks of
+  // PQ_CHUNK documents need, the documents are cut into about R * workgroups equal chunks,
+  // so no round runs with most workgroups idle (100K documents on 256 CUs: 7 rounds of 56
+  // documents instead of 6.1 rounds of 64, whose last round keeps 1 CU in 9 busy).
+  static const int fill = env_knob("MAXSIM_PQ_FILL", 1);  // 0: chunks of PQ_CHUNK, for measurements
+  const int64_t rounds = (a.n_docs + PQ_CHUNK * max_wg - 1) / (PQ_CHUNK * max_wg);
+  int64_t cd = rounds > 0 ? (a.n_docs + rounds * max_wg - 1) / (rounds * max_wg) : PQ_CHUNK;
+  if (!fill || cd > PQ_CHUNK) cd = PQ_CHUNK;
+  if (cd < 1) cd = 1;
+  PqScoreArgs ka = a;
+  ka.chunk_docs = (int)cd;
+  const int64_t nchunks = (a.n_docs + cd - 1) / cd;
   int64_t grid = nchunks < max_wg ? nchunks : max_wg;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(pq_score_kernel, dim3((unsigned)grid), dim3(PQ_THREADS), 0, st, a);
+  hipLaunchKernelGGL(pq_score_kernel, dim3((unsigned)grid), dim3(PQ_THREADS), 0, st, ka);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 

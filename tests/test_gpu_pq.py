@@ -86,6 +86,39 @@ def test_score_csr_ragged_with_empty_docs():
     compare(got, want, tol=PQ_TOL, what="PQ CSR")
 
 
+# The scorer cuts the documents into equal chunks of at most 64 that fill whole rounds of
+# the resident workgroups: at most 256 documents give chunks of 1 or 2 documents on 256 CUs,
+# so multi-document chunks (token runs that cross documents) need larger corpora. These
+# sizes give chunks of 64 (16384 documents), 33 (16385) and 53 (40000) on 256 CUs, and
+# multi-document chunks on any device of up to 304 CUs.
+@pytest.mark.parametrize("n_docs", [16384, 16385, 40000])
+def test_score_fixed_many_documents_per_chunk(n_docs):
+    say(f"case: PQ fixed n_docs={n_docs} nd=9 (documents per chunk > 1)")
+    C = gen.codebook(46)
+    Q = gen.tokens(46, gen.S_QUERY, 0, 32, 128, "bf16")
+    codes = gen.codes(46, n_docs * 9)
+    T = gpu_tables(Q, "bf16", C)
+    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, nd=9)
+    compare(gpu_pq(T, codes, nd=9), want, tol=PQ_TOL, what=f"PQ fixed B={n_docs}")
+
+
+def test_score_csr_many_documents_per_chunk():
+    """40000 CSR documents of 0 to 24 tokens (empty ones among them): chunks of about 53
+    documents whose token runs cross many document boundaries."""
+    lens = np.random.default_rng(47).integers(0, 25, size=40000).astype(np.int64)
+    lens[:5] = [0, 0, 24, 1, 0]
+    say(f"case: PQ CSR {len(lens)} short docs")
+    off = gen.csr_offsets(lens)
+    C = gen.codebook(47)
+    Q = gen.tokens(47, gen.S_QUERY, 0, 32, 128, "bf16")
+    codes = gen.codes(47, int(off[-1]))
+    T = gpu_tables(Q, "bf16", C)
+    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, offsets=off)
+    got = gpu_pq(T, codes, offsets=off)
+    assert np.all(np.isneginf(got[lens == 0]))
+    compare(got, want, tol=PQ_TOL, what="PQ CSR many short docs")
+
+
 def test_planted_docs_rank_first_after_encoding():
     """Planted near-duplicates stay on top after nearest-centroid PQ encoding."""
     say("case: PQ planted top-k")
