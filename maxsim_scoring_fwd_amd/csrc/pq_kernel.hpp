@@ -7,17 +7,19 @@
 // Codes are never expanded to vectors. The pages keep the table in on-chip
 // shared memory; on gfx950 the fp32 tables of 32 query tokens (512 KiB) exceed
 // the 160 KiB LDS, so the scorer stages one slice of 8 query tokens at a time.
-//  * A workgroup of 16 waves walks chunks of 64 documents. For each 8-query
-//    slice it copies T[slice] into LDS as TL[m][k][query] (the 8 queries of one
-//    (m, k) pair share 32 contiguous bytes). Two threads score each token, four
+//  * A workgroup of 16 waves owns a set of chunks of at most 64 documents (equal
+//    chunks sized so that they fill whole rounds of the resident workgroups). For
+//    each 8-query slice it copies T[slice] into LDS once, as TL[m][k][query] (the 8
+//    queries of one (m, k) pair share 32 contiguous bytes), and scores all its
+//    chunks (up to PQ_GROUP at a time) against it. Two threads score each token, four
 //    query tokens each: one 128-bit LDS read per subspace fetches four table
 //    entries, so a wave instruction serves 32 tokens.
 //  * Each thread pair scores a contiguous run of the chunk's tokens, keeping the
 //    running maxima of its four query tokens in registers; when the run crosses
 //    into another document the maxima are folded into mx[doc][query] with LDS
 //    float-max atomics. A max does not depend on order: scores are deterministic.
-//  * After each slice the chunk's per-document partial sums add the slice's
-//    maxima in query order; the chunk's scores are stored after the last slice.
+//  * After each slice each chunk's per-document partial sums add the slice's
+//    maxima in query order; the scores are stored after the last slice.
 //  * An empty document keeps -inf maxima and scores -inf.
 #pragma once
 
@@ -82,10 +84,16 @@ __global__ void __launch_bounds__(256) pq_tables_kernel(PqTableArgs a) {
   a.T[idx] = s;
 }
 
+// A workgroup owns the chunks blockIdx.x + r * gridDim.x. It stages each 8-query slice of
+// the tables once for up to PQ_GROUP of its chunks (instead of once per chunk), keeping
+// those chunks' per-document partial scores in LDS; each document's score still adds its
+// slices' sums in slice order, each sum in query order.
+constexpr int PQ_GROUP = 32;
+
 __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
   __shared__ __attribute__((aligned(16))) float tl[PQ_M * PQ_K * PQ_QS];  // 128 KiB: TL[m][k][query]
   __shared__ float mx[PQ_CHUNK * PQ_QS];        // maxima of the slice, per (document, query)
-  __shared__ float part[PQ_CHUNK];              // per-document partial scores
+  __shared__ float part[PQ_GROUP * PQ_CHUNK];   // partial scores of the group's documents
   __shared__ int32_t coff[PQ_CHUNK + 1];        // chunk-relative token offsets
   const int tid = threadIdx.x;
   const int pair = tid >> 1;                    // token lane: two threads per token
@@ -94,38 +102,21 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
   const int nslices = (q_len + PQ_QS - 1) / PQ_QS;
   const int cd = a.chunk_docs;
   const int64_t nchunks = (a.n_docs + cd - 1) / cd;
+  const int64_t mine = blockIdx.x < nchunks ? (nchunks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  // first document and document count of this workgroup's chunk r
+  auto chunk_docs = [&](int64_t r, int64_t &d0, int &ndc) {
+    d0 = ((int64_t)blockIdx.x + r * gridDim.x) * cd;
+    ndc = (int)(a.n_docs - d0 < cd ? a.n_docs - d0 : cd);
+  };
 
-  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
-    const int64_t d0 = ch * cd;
-    const int ndc = (int)(a.n_docs - d0 < cd ? a.n_docs - d0 : cd);
-    int64_t tok0;
-    __syncthreads();  // the previous chunk is done with coff and part
-    if (a.offsets) {
-      tok0 = a.offsets[d0];
-      if (tid <= ndc) coff[tid] = (int32_t)(a.offsets[d0 + tid] - tok0);
-    } else {
-      tok0 = d0 * (int64_t)a.nd;
-      if (tid <= ndc) coff[tid] = tid * a.nd;
-    }
-    if (tid < PQ_CHUNK) part[tid] = 0.f;
-    __syncthreads();
-
-    // this token lane's contiguous run of the chunk's tokens and the document holding
-    // its first token (largest doc with coff[doc] <= t_begin, skipping empty ones)
-    const int ntok = coff[ndc];
-    const int span = (ntok + PQ_PAIRS - 1) / PQ_PAIRS;
-    const int t_begin = pair * span < ntok ? pair * span : ntok;
-    const int t_end = t_begin + span < ntok ? t_begin + span : ntok;
-    int doc0 = 0;
-    for (int lo = 0, hi = ndc; lo < hi;) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (coff[mid] <= t_begin) lo = mid; else hi = mid - 1;
-      doc0 = lo;
-    }
+  for (int64_t g0 = 0; g0 < mine; g0 += PQ_GROUP) {
+    const int ng = (int)(mine - g0 < PQ_GROUP ? mine - g0 : PQ_GROUP);
+    __syncthreads();  // the previous group's scores have been stored
+    for (int i = tid; i < ng * PQ_CHUNK; i += PQ_THREADS) part[i] = 0.f;
 
     for (int sl = 0; sl < nslices; sl++) {
       const int q0 = sl * PQ_QS;
-      __syncthreads();  // the previous slice is done with tl and mx
+      __syncthreads();  // the previous slice is done with tl
       // TL[m][k][0..7] = T[q0 + 0..7][m][k]: one (m, k) row of 32 bytes per thread and
       // pass; neighbouring threads write neighbouring rows (no bank conflicts)
       for (int mk = tid; mk < PQ_M * PQ_K; mk += PQ_THREADS) {
@@ -138,49 +129,80 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
         *reinterpret_cast<f32x4_t *>(&tl[mk * PQ_QS]) = lo4;
         *reinterpret_cast<f32x4_t *>(&tl[mk * PQ_QS + 4]) = hi4;
       }
-      for (int idx = tid; idx < PQ_CHUNK * PQ_QS; idx += PQ_THREADS) mx[idx] = -__builtin_inff();
-      __syncthreads();
 
-      if (t_begin < t_end) {
-        int doc = doc0;
-        f32x4_t run = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-        u32x4_t cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t_begin) * PQ_M);
-        for (int t = t_begin; t < t_end; t++) {
-          const u32x4_t cur = cw;
-          if (t + 1 < t_end)  // next token's codes in flight while this one is scored
-            cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t + 1) * PQ_M);
-          if (t >= coff[doc + 1]) {
-            // this token starts a later document: fold the run into the finished one
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-            do doc++; while (coff[doc + 1] <= t);
-            run = f32x4_t{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-          }
-          f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < PQ_M; m++) {
-            const uint32_t k = (cur[m >> 2] >> ((m & 3) * 8)) & 0xffu;
-            s += *reinterpret_cast<const f32x4_t *>(&tl[(m * PQ_K + (int)k) * PQ_QS + 4 * h]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; e++) run[e] = __builtin_fmaxf(run[e], s[e]);
+      for (int r = 0; r < ng; r++) {
+        int64_t d0;
+        int ndc;
+        chunk_docs(g0 + r, d0, ndc);
+        int64_t tok0;
+        __syncthreads();  // the previous chunk is done with coff and mx
+        if (a.offsets) {
+          tok0 = a.offsets[d0];
+          if (tid <= ndc) coff[tid] = (int32_t)(a.offsets[d0 + tid] - tok0);
+        } else {
+          tok0 = d0 * (int64_t)a.nd;
+          if (tid <= ndc) coff[tid] = tid * a.nd;
         }
+        for (int idx = tid; idx < PQ_CHUNK * PQ_QS; idx += PQ_THREADS) mx[idx] = -__builtin_inff();
+        __syncthreads();  // coff, mx and the slice's table are ready
+
+        // this token lane's contiguous run of the chunk's tokens and the document holding
+        // its first token (largest doc with coff[doc] <= t_begin, skipping empty ones)
+        const int ntok = coff[ndc];
+        const int span = (ntok + PQ_PAIRS - 1) / PQ_PAIRS;
+        const int t_begin = pair * span < ntok ? pair * span : ntok;
+        const int t_end = t_begin + span < ntok ? t_begin + span : ntok;
+        if (t_begin < t_end) {
+          int doc = 0;
+          for (int lo = 0, hi = ndc; lo < hi;) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (coff[mid] <= t_begin) lo = mid; else hi = mid - 1;
+            doc = lo;
+          }
+          f32x4_t run = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+          u32x4_t cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t_begin) * PQ_M);
+          for (int t = t_begin; t < t_end; t++) {
+            const u32x4_t cur = cw;
+            if (t + 1 < t_end)  // next token's codes in flight while this one is scored
+              cw = load16(reinterpret_cast<const char *>(a.codes) + (tok0 + t + 1) * PQ_M);
+            if (t >= coff[doc + 1]) {
+              // this token starts a later document: fold the run into the finished one
 #pragma unroll
-        for (int e = 0; e < 4; e++)
-          __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      __syncthreads();
-      if (tid < ndc) {
-        float acc = 0.f;
-        for (int q = 0; q < PQ_QS && q0 + q < q_len; q++) acc += mx[tid * PQ_QS + q];
-        part[tid] += acc;
+              for (int e = 0; e < 4; e++)
+                __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+              do doc++; while (coff[doc + 1] <= t);
+              run = f32x4_t{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+            }
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < PQ_M; m++) {
+              const uint32_t k = (cur[m >> 2] >> ((m & 3) * 8)) & 0xffu;
+              s += *reinterpret_cast<const f32x4_t *>(&tl[(m * PQ_K + (int)k) * PQ_QS + 4 * h]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) run[e] = __builtin_fmaxf(run[e], s[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            __hip_atomic_fetch_max(&mx[doc * PQ_QS + 4 * h + e], run[e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        __syncthreads();  // the chunk's maxima for this slice are complete
+        if (tid < ndc) {
+          float acc = 0.f;
+          for (int q = 0; q < PQ_QS && q0 + q < q_len; q++) acc += mx[tid * PQ_QS + q];
+          part[r * PQ_CHUNK + tid] += acc;
+        }
       }
     }
     __syncthreads();
-    if (tid < ndc) a.out[d0 + tid] = part[tid];
+    for (int r = 0; r < ng; r++) {
+      int64_t d0;
+      int ndc;
+      chunk_docs(g0 + r, d0, ndc);
+      if (tid < ndc) a.out[d0 + tid] = part[r * PQ_CHUNK + tid];
+    }
   }
 }
 
