@@ -7,7 +7,7 @@
 // Codes are never expanded to vectors. The pages keep the table in on-chip
 // shared memory; on gfx950 the fp32 tables of 32 query tokens (512 KiB) exceed
 // the 160 KiB LDS, so the scorer stages one slice of 8 query tokens at a time.
-//  * A workgroup of 16 waves owns a set of chunks of at most 64 documents (equal
+//  * A workgroup of 16 waves owns a set of chunks of at most 512 documents (equal
 //    chunks sized so that they fill whole rounds of the resident workgroups). For
 //    each 8-query slice it copies T[slice] into LDS once, as TL[m][k][query] (the 8
 //    queries of one (m, k) pair share 32 contiguous bytes), and scores all its
@@ -34,7 +34,7 @@ constexpr int PQ_M = 16;
 constexpr int PQ_K = 256;
 constexpr int PQ_QS = 8;        // query tokens per LDS slice
 constexpr int PQ_THREADS = 1024;
-constexpr int PQ_CHUNK = 64;    // largest number of documents per chunk (LDS arrays)
+constexpr int PQ_CHUNK = 512;   // largest number of documents per chunk (LDS arrays)
 constexpr int PQ_PAIRS = PQ_THREADS / 2;  // token lanes per workgroup (two threads each)
 
 struct PqTableArgs {
@@ -88,7 +88,9 @@ __global__ void __launch_bounds__(256) pq_tables_kernel(PqTableArgs a) {
 // the tables once for up to PQ_GROUP of its chunks (instead of once per chunk), keeping
 // those chunks' per-document partial scores in LDS; each document's score still adds its
 // slices' sums in slice order, each sum in query order.
-constexpr int PQ_GROUP = 32;
+constexpr int PQ_GROUP = 4;
+// LDS: 128 KiB of table slice + maxima (PQ_CHUNK x 8 queries) + partial scores + offsets
+static_assert(PQ_CHUNK < PQ_THREADS, "one thread per chunk offset");
 
 __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
   __shared__ __attribute__((aligned(16))) float tl[PQ_M * PQ_K * PQ_QS];  // 128 KiB: TL[m][k][query]
@@ -223,8 +225,8 @@ inline int pq_score_run(const PqScoreArgs &a, const DeviceInfo &di, hipStream_t 
   const int64_t max_wg = (int64_t)bpc * di.cus;
   // Chunks fill whole rounds of the resident workgroups: with R the rounds that chunks of
   // PQ_CHUNK documents need, the documents are cut into about R * workgroups equal chunks,
-  // so no round runs with most workgroups idle (100K documents on 256 CUs: 7 rounds of 56
-  // documents instead of 6.1 rounds of 64, whose last round keeps 1 CU in 9 busy).
+  // so no round runs with most workgroups idle (100K documents on 256 CUs: one round of
+  // 391-document chunks).
   static const int fill = env_knob("MAXSIM_PQ_FILL", 1);  // 0: chunks of PQ_CHUNK, for measurements
   const int64_t rounds = (a.n_docs + PQ_CHUNK * max_wg - 1) / (PQ_CHUNK * max_wg);
   int64_t cd = rounds > 0 ? (a.n_docs + rounds * max_wg - 1) / (rounds * max_wg) : PQ_CHUNK;

@@ -86,10 +86,10 @@ def test_score_csr_ragged_with_empty_docs():
     compare(got, want, tol=PQ_TOL, what="PQ CSR")
 
 
-# The scorer cuts the documents into equal chunks of at most 64 that fill whole rounds of
-# the resident workgroups: at most 256 documents give chunks of 1 or 2 documents on 256 CUs,
-# so multi-document chunks (token runs that cross documents) need larger corpora. These
-# sizes give chunks of 64 (16384 documents), 33 (16385) and 53 (40000) on 256 CUs, and
+# The scorer cuts the documents into equal chunks of at most 512 that fill whole rounds of
+# the resident workgroups: at most 256 documents give chunks of 1 document on 256 CUs, so
+# multi-document chunks (token runs that cross documents) need larger corpora. These sizes
+# give chunks of 64 (16384 documents), 65 (16385) and 157 (40000) on 256 CUs, and
 # multi-document chunks on any device of up to 304 CUs.
 @pytest.mark.parametrize("n_docs", [16384, 16385, 40000])
 def test_score_fixed_many_documents_per_chunk(n_docs):
@@ -103,7 +103,7 @@ def test_score_fixed_many_documents_per_chunk(n_docs):
 
 
 def test_score_csr_many_documents_per_chunk():
-    """40000 CSR documents of 0 to 24 tokens (empty ones among them): chunks of about 53
+    """40000 CSR documents of 0 to 24 tokens (empty ones among them): chunks of about 157
     documents whose token runs cross many document boundaries."""
     lens = np.random.default_rng(47).integers(0, 25, size=40000).astype(np.int64)
     lens[:5] = [0, 0, 24, 1, 0]
