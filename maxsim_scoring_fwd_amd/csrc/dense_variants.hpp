@@ -52,6 +52,12 @@ int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipSt
       if (mode == LOAD_DIRECT_NT)
         return launch_dense<DT, KSB, QB, 8, QLDS, LOAD_DIRECT_NT, ARG>(a, lds, di, st);
     }
+    // CSR corpora: token-balanced ranges end on document boundaries, so a wave whose range
+    // ends inside a long document finishes last, alone; a deeper ring shortens that tail
+    // (measured depth 4 / 6 / 10 / 12: 80.5-80.7 / 80.7-81.0 / 81.2-81.4 / 81.8-81.9% of
+    // HBM peak on the lognormal corpus). 12 is the deepest ring at two waves per SIMD.
+    if (a.offsets && depth == 0)
+      return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
     if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
     if (depth == 6) return launch_dense<DT, KSB, QB, 6, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
     if (depth == 10) return launch_dense<DT, KSB, QB, 10, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
