@@ -7,11 +7,11 @@
 // Codes are never expanded to vectors. The pages keep the table in on-chip
 // shared memory; on gfx950 the fp32 tables of 32 query tokens (512 KiB) exceed
 // the 160 KiB LDS, so the scorer stages one slice of 8 query tokens at a time.
-//  * A workgroup of 16 waves owns a set of chunks of at most 512 documents (equal
-//    chunks sized so that they fill whole rounds of the resident workgroups). For
-//    each 8-query slice it copies T[slice] into LDS once, as TL[m][k][query] (the 8
-//    queries of one (m, k) pair share 32 contiguous bytes), and scores all its
-//    chunks (up to PQ_GROUP at a time) against it. Two threads score each token, four
+//  * A workgroup of 16 waves owns one contiguous range of documents (token-balanced
+//    for CSR corpora), cut into equal chunks of at most 512 documents. For each
+//    8-query slice it copies T[slice] into LDS once, as TL[m][k][query] (the 8
+//    queries of one (m, k) pair share 32 contiguous bytes), and scores its chunks
+//    (up to PQ_GROUP at a time) against it. Two threads score each token, four
 //    query tokens each: one 128-bit LDS read per subspace fetches four table
 //    entries, so a wave instruction serves 32 tokens.
 //  * Each thread pair scores a contiguous run of the chunk's tokens, keeping the
@@ -54,7 +54,6 @@ struct PqScoreArgs {
   int64_t n_docs;
   int nd;
   float *out;
-  int chunk_docs = PQ_CHUNK;  // documents per chunk, 1 .. PQ_CHUNK
 };
 
 template <int DT> __device__ __forceinline__ float decode_elem(const char *Q, int64_t idx);
@@ -84,10 +83,12 @@ __global__ void __launch_bounds__(256) pq_tables_kernel(PqTableArgs a) {
   a.T[idx] = s;
 }
 
-// A workgroup owns the chunks blockIdx.x + r * gridDim.x. It stages each 8-query slice of
-// the tables once for up to PQ_GROUP of its chunks (instead of once per chunk), keeping
-// those chunks' per-document partial scores in LDS; each document's score still adds its
-// slices' sums in slice order, each sum in query order.
+// A workgroup owns one contiguous range of documents: a token-balanced range for CSR
+// documents (those starting in its share of the tokens, as in the dense kernel), an equal
+// share of fixed-length documents otherwise. The range is cut into equal chunks of at most
+// PQ_CHUNK documents. The workgroup stages each 8-query slice of the tables once for up to
+// PQ_GROUP of its chunks, keeping their per-document partial scores in LDS; each
+// document's score still adds its slices' sums in slice order, each sum in query order.
 constexpr int PQ_GROUP = 4;
 // LDS: 128 KiB of table slice + maxima (PQ_CHUNK x 8 queries) + partial scores + offsets
 static_assert(PQ_CHUNK < PQ_THREADS, "one thread per chunk offset");
@@ -98,17 +99,32 @@ __global__ void __launch_bounds__(PQ_THREADS) pq_score_kernel(PqScoreArgs a) {
   __shared__ float part[PQ_GROUP * PQ_CHUNK];   // partial scores of the group's documents
   __shared__ int32_t coff[PQ_CHUNK + 1];        // chunk-relative token offsets
   const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
   const int pair = tid >> 1;                    // token lane: two threads per token
   const int h = tid & 1;                        // which 4 of the slice's 8 query tokens
   const int q_len = a.q_len;
   const int nslices = (q_len + PQ_QS - 1) / PQ_QS;
-  const int cd = a.chunk_docs;
-  const int64_t nchunks = (a.n_docs + cd - 1) / cd;
-  const int64_t mine = blockIdx.x < nchunks ? (nchunks - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int64_t wg = blockIdx.x, nwg = gridDim.x;
+  // this workgroup's documents [rb, re) (every wave computes the same range)
+  int64_t rb, re;
+  if (a.offsets) {
+    const int64_t t0 = uniform(a.offsets[0]);
+    const int64_t ntok = uniform(a.offsets[a.n_docs]) - t0;
+    const int64_t lo = t0 + ntok * wg / nwg, hi = t0 + ntok * (wg + 1) / nwg;
+    rb = wg == 0 ? 0 : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, lo, lane));
+    re = wg == nwg - 1 ? a.n_docs : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, hi, lane));
+  } else {
+    rb = a.n_docs * wg / nwg;
+    re = a.n_docs * (wg + 1) / nwg;
+  }
+  const int64_t nr = re > rb ? re - rb : 0;
+  const int64_t mine = (nr + PQ_CHUNK - 1) / PQ_CHUNK;  // chunks of the range
+  const int64_t cd = mine > 0 ? (nr + mine - 1) / mine : 1;  // documents per chunk (equal split)
   // first document and document count of this workgroup's chunk r
   auto chunk_docs = [&](int64_t r, int64_t &d0, int &ndc) {
-    d0 = ((int64_t)blockIdx.x + r * gridDim.x) * cd;
-    ndc = (int)(a.n_docs - d0 < cd ? a.n_docs - d0 : cd);
+    d0 = rb + r * cd;
+    const int64_t left = re - d0;
+    ndc = (int)(left < cd ? (left > 0 ? left : 0) : cd);
   };
 
   for (int64_t g0 = 0; g0 < mine; g0 += PQ_GROUP) {
@@ -221,23 +237,13 @@ inline int pq_tables_run(const PqTableArgs &a, const DeviceInfo &, hipStream_t s
 }
 
 inline int pq_score_run(const PqScoreArgs &a, const DeviceInfo &di, hipStream_t st) {
+  // One workgroup per CU (the table slice fills LDS), each with one contiguous range of
+  // documents: one round, balanced by tokens for CSR corpora.
   const int bpc = blocks_per_cu((const void *)pq_score_kernel, PQ_THREADS, 0);
   const int64_t max_wg = (int64_t)bpc * di.cus;
-  // Chunks fill whole rounds of the resident workgroups: with R the rounds that chunks of
-  // PQ_CHUNK documents need, the documents are cut into about R * workgroups equal chunks,
-  // so no round runs with most workgroups idle (100K documents on 256 CUs: one round of
-  // 391-document chunks).
-  static const int fill = env_knob("MAXSIM_PQ_FILL", 1);  // 0: chunks of PQ_CHUNK, for measurements
-  const int64_t rounds = (a.n_docs + PQ_CHUNK * max_wg - 1) / (PQ_CHUNK * max_wg);
-  int64_t cd = rounds > 0 ? (a.n_docs + rounds * max_wg - 1) / (rounds * max_wg) : PQ_CHUNK;
-  if (!fill || cd > PQ_CHUNK) cd = PQ_CHUNK;
-  if (cd < 1) cd = 1;
-  PqScoreArgs ka = a;
-  ka.chunk_docs = (int)cd;
-  const int64_t nchunks = (a.n_docs + cd - 1) / cd;
-  int64_t grid = nchunks < max_wg ? nchunks : max_wg;
+  int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(pq_score_kernel, dim3((unsigned)grid), dim3(PQ_THREADS), 0, st, ka);
+  hipLaunchKernelGGL(pq_score_kernel, dim3((unsigned)grid), dim3(PQ_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 

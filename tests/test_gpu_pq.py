@@ -86,28 +86,31 @@ def test_score_csr_ragged_with_empty_docs():
     compare(got, want, tol=PQ_TOL, what="PQ CSR")
 
 
-# The scorer cuts the documents into equal chunks of at most 512 that fill whole rounds of
-# the resident workgroups: at most 256 documents give chunks of 1 document on 256 CUs, so
-# multi-document chunks (token runs that cross documents) need larger corpora. These sizes
-# give chunks of 64 (16384 documents), 65 (16385) and 157 (40000) on 256 CUs, and
-# multi-document chunks on any device of up to 304 CUs.
-@pytest.mark.parametrize("n_docs", [16384, 16385, 40000])
-def test_score_fixed_many_documents_per_chunk(n_docs):
-    say(f"case: PQ fixed n_docs={n_docs} nd=9 (documents per chunk > 1)")
+# The scorer gives each workgroup (one per CU) a contiguous range of documents, balanced by
+# tokens for CSR corpora, cut into equal chunks of at most 512 documents, and stages each
+# table slice once for up to 4 of its chunks. On 256 CUs: 16384 and 16385 documents give one
+# chunk of 64-65 documents per workgroup, 40000 give 156-157, 140000 give two chunks of about
+# 273, and 600000 give five chunks of about 469 (two groups of chunks per slice staging).
+@pytest.mark.parametrize("n_docs,nd", [(16384, 9), (16385, 9), (40000, 9), (140000, 2),
+                                       (600000, 1)])
+def test_score_fixed_many_documents_per_chunk(n_docs, nd):
+    say(f"case: PQ fixed n_docs={n_docs} nd={nd} (documents per chunk > 1)")
     C = gen.codebook(46)
     Q = gen.tokens(46, gen.S_QUERY, 0, 32, 128, "bf16")
-    codes = gen.codes(46, n_docs * 9)
+    codes = gen.codes(46, n_docs * nd)
     T = gpu_tables(Q, "bf16", C)
-    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, nd=9)
-    compare(gpu_pq(T, codes, nd=9), want, tol=PQ_TOL, what=f"PQ fixed B={n_docs}")
+    want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, nd=nd)
+    compare(gpu_pq(T, codes, nd=nd), want, tol=PQ_TOL, what=f"PQ fixed B={n_docs} nd={nd}")
 
 
-def test_score_csr_many_documents_per_chunk():
-    """40000 CSR documents of 0 to 24 tokens (empty ones among them): chunks of about 157
-    documents whose token runs cross many document boundaries."""
-    lens = np.random.default_rng(47).integers(0, 25, size=40000).astype(np.int64)
-    lens[:5] = [0, 0, 24, 1, 0]
-    say(f"case: PQ CSR {len(lens)} short docs")
+@pytest.mark.parametrize("n_docs,max_len", [(40000, 24), (200000, 3)])
+def test_score_csr_many_documents_per_chunk(n_docs, max_len):
+    """Many short CSR documents (empty ones among them): token-balanced workgroup ranges of
+    about 156 (40000 documents) or 780 (200000, two chunks per workgroup) documents whose
+    token runs cross many document boundaries."""
+    lens = np.random.default_rng(47 + max_len).integers(0, max_len + 1, size=n_docs).astype(np.int64)
+    lens[:5] = [0, 0, max_len, 1, 0]
+    say(f"case: PQ CSR {len(lens)} short docs (at most {max_len} tokens)")
     off = gen.csr_offsets(lens)
     C = gen.codebook(47)
     Q = gen.tokens(47, gen.S_QUERY, 0, 32, 128, "bf16")
@@ -116,7 +119,7 @@ def test_score_csr_many_documents_per_chunk():
     want = oracle.maxsim_pq(oracle.pq_tables(Q, "bf16", C), codes, offsets=off)
     got = gpu_pq(T, codes, offsets=off)
     assert np.all(np.isneginf(got[lens == 0]))
-    compare(got, want, tol=PQ_TOL, what="PQ CSR many short docs")
+    compare(got, want, tol=PQ_TOL, what=f"PQ CSR {n_docs} short docs")
 
 
 def test_planted_docs_rank_first_after_encoding():
