@@ -28,6 +28,11 @@ int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di
   // override both for measurements.
   static const int nt = env_knob("MAXSIM_BWD_NT", 1);
   static const int wgs = env_knob("MAXSIM_BWD_WGS", -1);
+  // CSR ranges balance 64 tokens per document plus one per token: the per-document phases
+  // (counting, scan, placement) cost about as much as writing 64 gradient rows (measured
+  // weights 0 / 16 / 32 / 64 / 128: 0.466 / 0.459-0.460 / 0.453-0.457 / 0.453-0.457 /
+  // 0.453-0.454 ms at the lognormal corpus). MAXSIM_BWD_DOC_WEIGHT overrides it.
+  static const int doc_weight = env_knob("MAXSIM_BWD_DOC_WEIGHT", 64);
   auto kern = nt ? bwd_dd_kernel<DT, OT, QLDS, true> : bwd_dd_kernel<DT, OT, QLDS, false>;
   const size_t lds = (size_t)q_lds + (size_t)BWD_WAVES * bwd_dd_wave_ints(seg_cap, a.q_len) * 4;
   if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
@@ -38,7 +43,9 @@ int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di
   const int64_t need = (a.n_docs + BWD_WAVES - 1) / BWD_WAVES;
   int64_t grid = need < max_wg ? need : max_wg;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), lds, st, a, seg_cap, q_lds);
+  BwdArgs ka = a;
+  ka.doc_weight = doc_weight;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), lds, st, ka, seg_cap, q_lds);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 

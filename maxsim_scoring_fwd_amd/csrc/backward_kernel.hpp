@@ -49,6 +49,7 @@ struct BwdArgs {
   char *dD;                // [tokens][d] in the gradient type
   float *partial;          // dQ partial sums: [n_ranges][q_len * d]
   int n_ranges;
+  int doc_weight = 0;      // dD over CSR documents: per-document cost in tokens for balancing
 };
 
 constexpr int BWD_THREADS = 256;
@@ -136,6 +137,26 @@ __device__ __forceinline__ void store_chunk(char *p, const float (&x)[E]) {
     *reinterpret_cast<u32x4_t *>(p) = v;
 }
 
+// First index i in [0, n) with (off[i] - t0) + w * i >= target, or n if none: the lower
+// bound of a target in the cumulative cost of documents [0, i) when a document costs w plus
+// one per token (off non-decreasing). 64 probes per round, as wave_lower_bound.
+__device__ __forceinline__ int64_t weighted_lower_bound(const int64_t *off, int64_t n, int64_t t0,
+                                                        int64_t w, int64_t target, int lane) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t step = (hi - lo + WAVE - 1) / WAVE;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool less = idx < hi && off[idx] - t0 + w * idx < target;
+    const int cnt = __popcll(__ballot(less));
+    if (cnt == 0) return lo;
+    const int64_t last_less = lo + (int64_t)(cnt - 1) * step;
+    const int64_t next = last_less + step;
+    lo = uniform(last_less + 1);
+    hi = uniform(next < hi ? next : hi);
+  }
+  return lo;
+}
+
 // Dynamic LDS of the dD kernel: the query as stored (QLDS) at offset 0, then per wave
 // cnt[seg_cap], off[seg_cap + 1] and idx[q_len] (int32).
 __host__ __device__ inline int bwd_dd_wave_ints(int seg_cap, int q_len) {
@@ -180,15 +201,17 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a, int seg_
       load_f32<DT, E>(a.Q + o, x);
   };
 
-  // documents of this wave: a token-balanced contiguous range (CSR) or a stride
+  // documents of this wave: a contiguous range (CSR) balanced on doc_weight per document
+  // plus one per token, or a stride
   int64_t b = wave, bend = a.n_docs, bstep = nwaves;
   if (a.offsets) {
     const int64_t t0 = uniform(a.offsets[0]);
-    const int64_t ntok = uniform(a.offsets[a.n_docs]) - t0;
-    const int64_t lo = t0 + ntok * wave / nwaves, hi = t0 + ntok * (wave + 1) / nwaves;
-    b = wave == 0 ? 0 : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, lo, lane));
+    const int64_t w = a.doc_weight;
+    const int64_t total = uniform(a.offsets[a.n_docs]) - t0 + w * a.n_docs;
+    const int64_t lo = total * wave / nwaves, hi = total * (wave + 1) / nwaves;
+    b = wave == 0 ? 0 : uniform(weighted_lower_bound(a.offsets, a.n_docs + 1, t0, w, lo, lane));
     bend = wave == nwaves - 1 ? a.n_docs
-                              : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, hi, lane));
+                              : uniform(weighted_lower_bound(a.offsets, a.n_docs + 1, t0, w, hi, lane));
     bstep = 1;
   }
 
