@@ -399,9 +399,16 @@ def cpu_baseline(w, budget_s: float):
     n = int(min(w["B"], max(n0, n0 * budget_s / max(t0, 1e-6))))
     t = score(n) if n > n0 else t0
     unit = "docs/s" if n_q == 1 else "(query, document) scores/s"
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(n_q * n / t, 1), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {w['B']} documents of the same workload "
-                      f"(float64 oracle, {t:.1f} s)"}
+                      f"(float64 oracle, {t:.1f} s)",
+            "cpu_model": model, "host_cpus_visible": os.cpu_count()}
 
 
 def copy_probe(mib: int, steps: int):
