@@ -211,8 +211,9 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   constexpr bool PIPE = QBW * KSB <= 16 && (I8 || NW == 4);
   // The 8-wave dense instances of the several-query pass pipeline by halves of the query
   // slice (no extra registers). Measured: 32 ColBERT queries +6%; the single long query
-  // (ColPali shape, the same loop) -3%, so it keeps the plain loop.
-  constexpr bool HALF = BATCH && !PIPE && !I8 && NW >= TILED_WAVES && QBW % 2 == 0;
+  // (ColPali shape, the same loop) -3%, so it keeps the plain loop, except with the argmax,
+  // whose fold is heavier (a compare and two selects per similarity): +1-2% there.
+  constexpr bool HALF = (BATCH || ARG) && !PIPE && !I8 && NW >= TILED_WAVES && QBW % 2 == 0;
   using AccT = typename AccType<I8>::type;
 
   // Several queries whose blocks never straddle two waves ("local"): each segment of a wave
