@@ -261,6 +261,12 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     pend_q = -1;
   };
 
+  // byte offset of this lane's A-operand piece c within a staged 16-row tile
+  int a_off[KSB];
+#pragma unroll
+  for (int c = 0; c < KSB; c++)
+    a_off[c] = (r16 * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(r16))) * 16;
+
   while (meta.b < a.n_docs) {
     // this block: stage the prefetched pieces in LDS
     char *tile = blk_lds[buf];
@@ -298,10 +304,10 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
       const int64_t rows_left = len - (int64_t)blk * BLK_ROWS;
       const int ntiles = rows_left >= BLK_ROWS ? BLK_TILES : (int)((rows_left + 15) >> 4);
       // A operand of chunk c of tile t: row t * 16 + r16, pieces 4c .. 4c + 3
+      // (row t * 16 + r16 has the swizzle of row r16, so the lane's offset within a tile,
+      // a_off[c], is fixed and tile t adds t * 16 rows)
       auto read_a = [&](int t, int c) -> u32x4_t {
-        const int row = t * 16 + r16;
-        return *reinterpret_cast<const u32x4_t *>(
-            tile + (row * PPR + ((4 * c + g) ^ stage_swizzle<PPR>(row))) * 16);
+        return *reinterpret_cast<const u32x4_t *>(tile + t * (16 * PPR * 16) + a_off[c]);
       };
       // all query blocks' accumulators are live: consecutive MFMAs are independent
       auto mfma_tile = [&](AccT(&acc)[QBW], const u32x4_t(&aop)[KSB]) {
