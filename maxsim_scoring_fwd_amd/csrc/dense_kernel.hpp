@@ -128,6 +128,22 @@ __device__ __forceinline__ int64_t wave_lower_bound(const int64_t *off, int64_t 
   return lo;
 }
 
+// The document boundary nearest to token target: the first document starting at or after
+// target, or the one before it when that starts closer below (wave-uniform). Neighbouring
+// waves cut their ranges with the same rule, so every document belongs to one wave, and a
+// long document straddling a cut adds at most half its length to either wave.
+__device__ __forceinline__ int64_t nearest_boundary(const int64_t *off, int64_t n_docs,
+                                                    int64_t target, int lane) {
+  int64_t b = uniform(wave_lower_bound(off, n_docs + 1, target, lane));
+  if (b > 0) {
+    const c_i64 *o = (const c_i64 *)off;
+    const int64_t below = uniform(o[b - 1]);
+    const int64_t above = b <= n_docs ? uniform(o[b]) : below;
+    if (b > n_docs || target - below < above - target) b--;
+  }
+  return b;
+}
+
 // Per-slot state of the load ring (wave-uniform). The flags are kept as separate
 // booleans: packed into one integer they lead the compiler to wait for every
 // load in flight before each tile, which serialises the ring.
@@ -192,8 +208,8 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
     const int64_t t0 = uniform(a.offsets[0]);
     const int64_t ntok = uniform(a.offsets[a.n_docs]) - t0;
     const int64_t lo = t0 + ntok * wave / nwaves, hi = t0 + ntok * (wave + 1) / nwaves;
-    pb = uniform(wave_lower_bound(a.offsets, a.n_docs + 1, lo, lane));
-    pend = wave == nwaves - 1 ? a.n_docs : uniform(wave_lower_bound(a.offsets, a.n_docs + 1, hi, lane));
+    pb = nearest_boundary(a.offsets, a.n_docs, lo, lane);
+    pend = wave == nwaves - 1 ? a.n_docs : nearest_boundary(a.offsets, a.n_docs, hi, lane);
     if (wave == 0) pb = 0;
     pstep = 1;
   } else if (a.contiguous) {
