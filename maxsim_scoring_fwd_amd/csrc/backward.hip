@@ -33,6 +33,13 @@ int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di
   // weights 0 / 16 / 32 / 64 / 128: 0.466 / 0.459-0.460 / 0.453-0.457 / 0.453-0.457 /
   // 0.453-0.454 ms at the lognormal corpus). MAXSIM_BWD_DOC_WEIGHT overrides it.
   static const int doc_weight = env_knob("MAXSIM_BWD_DOC_WEIGHT", 64);
+  // Chosen-token sets for queries of at most 64 tokens (query in LDS): CSR dD measured
+  // 0.429 against 0.454 ms at the lognormal corpus; fixed 128-token documents, capped at two
+  // workgroups per CU, measured 0.640 against 0.591 ms, so they keep the counting path.
+  // Prefetching the next document measured the same as loading it after the stores.
+  // MAXSIM_BWD_SETS overrides (0 off, 1 sets, 3 sets without prefetch).
+  static const int sets_knob = env_knob("MAXSIM_BWD_SETS", -1);
+  const int short_sets = sets_knob >= 0 ? sets_knob : (a.offsets ? 1 : 0);
   auto kern = nt ? bwd_dd_kernel<DT, OT, QLDS, true> : bwd_dd_kernel<DT, OT, QLDS, false>;
   const size_t lds = (size_t)q_lds + (size_t)BWD_WAVES * bwd_dd_wave_ints(seg_cap, a.q_len) * 4;
   if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
@@ -45,6 +52,7 @@ int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di
   if (grid < 1) grid = 1;
   BwdArgs ka = a;
   ka.doc_weight = doc_weight;
+  ka.short_sets = short_sets;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), lds, st, ka, seg_cap, q_lds);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }

@@ -50,6 +50,8 @@ struct BwdArgs {
   float *partial;          // dQ partial sums: [n_ranges][q_len * d]
   int n_ranges;
   int doc_weight = 0;      // dD over CSR documents: per-document cost in tokens for balancing
+  int short_sets = 1;      // dD, query in LDS, q_len <= 64: bit 0 chosen-token sets, bit 1
+                           // no prefetch of the next document
 };
 
 constexpr int BWD_THREADS = 256;
@@ -214,6 +216,76 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a, int seg_
     bend = wave == nwaves - 1 ? a.n_docs
                               : uniform(weighted_lower_bound(a.offsets, a.n_docs + 1, t0, w, hi, lane));
     bstep = 1;
+  }
+
+  if constexpr (QLDS) {
+    if (q_len <= WAVE && (a.short_sets & 1)) {
+      // Short queries, one token per lane: the query tokens that chose a row form a 64-bit
+      // set (low word in cnt, high word in off), built with one LDS OR per token and walked
+      // lowest bit first, so every row's sum keeps increasing query order (0 + first +
+      // second ...), as in the general path, with no counting, scan or placement phase.
+      // The next document's extent, weight and choices load while this one is written.
+      uint32_t *lo = reinterpret_cast<uint32_t *>(cnt), *hi = reinterpret_cast<uint32_t *>(off);
+      auto fetch = [&](int64_t bb, int64_t &f, int64_t &l, float &gg, int &k) {
+        bwd_extent(a, bb, f, l);
+        gg = a.grad[bb];
+        k = lane < q_len ? a.tok_arg[bb * q_len + lane] : -1;
+      };
+      int64_t first = 0, len = 0;
+      float g = 0.f;
+      int key = -1;
+      const bool pre = !(a.short_sets & 2);
+      if (b < bend) fetch(b, first, len, g, key);
+      for (; b < bend; b += bstep) {
+        int64_t nfirst = 0, nlen = 0;
+        float ng = 0.f;
+        int nkey = -1;
+        if (pre && b + bstep < bend) fetch(b + bstep, nfirst, nlen, ng, nkey);
+        for (int64_t s0 = 0; s0 < len; s0 += seg_cap) {
+          const int seg = (int)(len - s0 < seg_cap ? len - s0 : seg_cap);
+          for (int j = lane; j < seg; j += WAVE) {
+            lo[j] = 0u;
+            hi[j] = 0u;
+          }
+          wave_lds_sync();
+          const int64_t j = (int64_t)key - s0;
+          if (j >= 0 && j < seg)
+            __hip_atomic_fetch_or(lane < 32 ? &lo[j] : &hi[j], 1u << (lane & 31),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+          wave_lds_sync();
+          char *dst = a.dD + (first + s0) * (int64_t)d * OB;
+          auto emit = [&](int row, int c) {
+            uint64_t m = ((uint64_t)hi[row] << 32) | lo[row];
+            float acc[E];
+#pragma unroll
+            for (int k = 0; k < E; k++) acc[k] = 0.f;
+            while (m) {
+              const int i = __builtin_ctzll(m);
+              m &= m - 1;
+              float x[E];
+              q_chunk(i, c, x);
+#pragma unroll
+              for (int k = 0; k < E; k++) acc[k] += x[k];
+            }
+#pragma unroll
+            for (int k = 0; k < E; k++) acc[k] *= g;
+            store_chunk<OT, E, NT>(dst + ((int64_t)row * cpr + c) * 16, acc);
+          };
+          if (by_row) {
+            for (int row = my_r; row < seg; row += rpi) emit(row, my_c);
+          } else {
+            for (int u = lane; u < seg * cpr; u += WAVE) emit(u / cpr, u % cpr);
+          }
+          wave_lds_sync();  // the next segment reuses the wave's LDS
+        }
+        if (!pre && b + bstep < bend) fetch(b + bstep, nfirst, nlen, ng, nkey);
+        first = nfirst;
+        len = nlen;
+        g = ng;
+        key = nkey;
+      }
+      return;
+    }
   }
 
   for (; b < bend; b += bstep) {

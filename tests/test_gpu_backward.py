@@ -235,18 +235,20 @@ def test_backward_fixed(dtype, grad_dtype):
     check_backward(c, g, gd, "fixed")
 
 
+@pytest.mark.parametrize("q_len", [32, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_backward_csr_long_and_empty_documents(dtype):
-    """Documents longer than one inverse-grid segment (1024 tokens), empty documents and
-    a ragged tail."""
+def test_backward_csr_long_and_empty_documents(dtype, q_len):
+    """Documents longer than one inverse-grid segment (256 tokens), empty documents and
+    a ragged tail; with 64 query tokens every lane of the chosen-token sets is used."""
     lens = np.concatenate([[0, 2500, 1, 0, 1024, 1025], gen.lengths(610, 40)])
-    say(f"case: backward CSR {dtype} {len(lens)} docs incl. 2500 tokens and empty")
-    c = gen.csr_corpus(610, len(lens), 32, 128, dtype, lens=lens)
+    say(f"case: backward CSR {dtype} q_len={q_len} {len(lens)} docs incl. 2500 tokens and empty")
+    c = gen.csr_corpus(610, len(lens), q_len, 128, dtype, lens=lens)
     g = np.random.default_rng(610).standard_normal(len(lens)).astype(np.float32)
     check_backward(c, g, "fp32", "csr")
 
 
-@pytest.mark.parametrize("q_len,d", [(1024, 128), (1000, 64), (100, 768), (64, 256), (1, 128)])
+@pytest.mark.parametrize("q_len,d", [(1024, 128), (1000, 64), (100, 768), (64, 256), (1, 128),
+                                       (24, 768), (48, 384)])
 def test_backward_query_shapes(q_len, d):
     say(f"case: backward q_len={q_len} d={d} bf16")
     c = gen.fixed_corpus(620 + q_len + d, 5, q_len, 150, d, "bf16")
