@@ -68,8 +68,14 @@ int launch_dd(const BwdArgs &a, const DeviceInfo &di, hipStream_t st) {
 template <int DT, int OT>
 int launch_dq(const BwdArgs &a, hipStream_t st) {
   const unsigned blocks = (unsigned)((a.q_len * a.d + DQ_ELEMS_PER_WG - 1) / DQ_ELEMS_PER_WG);
-  hipLaunchKernelGGL(bwd_dq_partial_kernel<DT>, dim3(blocks, (unsigned)a.n_ranges),
-                     dim3(BWD_THREADS), 0, st, a);
+  // Documents in flight per step of a thread; MAXSIM_BWD_DQ_DOCS (1, 2, 3, 4 or 8) overrides.
+  static const int docs = env_knob("MAXSIM_BWD_DQ_DOCS", DQ_DOCS);
+  auto kern = docs == 8   ? bwd_dq_partial_kernel<DT, 8>
+              : docs == 3 ? bwd_dq_partial_kernel<DT, 3>
+              : docs == 2 ? bwd_dq_partial_kernel<DT, 2>
+              : docs == 1 ? bwd_dq_partial_kernel<DT, 1>
+                          : bwd_dq_partial_kernel<DT, 4>;
+  hipLaunchKernelGGL(kern, dim3(blocks, (unsigned)a.n_ranges), dim3(BWD_THREADS), 0, st, a);
   if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
   const int n_elem = a.q_len * a.d;
   const unsigned rblocks = (unsigned)((n_elem + RED_ELEMS - 1) / RED_ELEMS);

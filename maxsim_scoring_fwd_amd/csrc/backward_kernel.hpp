@@ -19,7 +19,9 @@
 //    rows; a chunk sums its row's query tokens in that fixed order and scales by
 //    g_b once; the query is read from LDS when it fits. Long documents are processed
 //    in segments of at most BWD_SEG tokens. CSR documents are split into token-balanced
-//    contiguous ranges across waves.
+//    contiguous ranges across waves. For CSR queries of at most 64 tokens the grid is a
+//    64-bit set of query tokens per row instead (one LDS OR per token, walked lowest bit
+//    first: the same summation order).
 //  * dQ (gathers q_len document rows per document). Each workgroup owns a block
 //    of 4-element chunks of dQ and a contiguous range of documents, and adds
 //    g_b times the chosen rows in document order into registers; the partial
@@ -59,7 +61,10 @@ constexpr int BWD_WAVES = BWD_THREADS / WAVE;
 constexpr int BWD_SEG = 1024;  // longest inverse-grid segment (document tokens)
 constexpr int BWD_Q_LDS_MAX = 48 * 1024;  // largest query copied to LDS (bytes)
 constexpr int DQ_ELEMS_PER_WG = 4096;  // dQ elements per workgroup (16-byte chunks per thread)
-constexpr int DQ_DOCS = 4;             // documents in flight per step
+// Documents in flight per step of a dQ thread. Measured at the ColBERT shape (dQ partial,
+// CSR corpus / fixed Nd=128): 1, 2, 3, 4, 8 gave 147 / 137 / 134 / 179 / 175 us and
+// 153 / 147 / 146 / 186 / 180 us, every instance at 8 waves per SIMD.
+constexpr int DQ_DOCS = 3;
 constexpr int DD_ROWS = 4;             // dD rows per lane with their gathers in flight
 
 __device__ __forceinline__ void bwd_extent(const BwdArgs &a, int64_t b, int64_t &first,
@@ -418,7 +423,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a, int seg_
 // dQ partial sums: grid (element blocks, document ranges). Each thread owns SLOTS chunks
 // of 16 bytes of the stored type (E elements each) of dQ and adds g_b times the chosen
 // rows' chunks for the documents of its range, in document order.
-template <int DT>
+template <int DT, int DOCS = DQ_DOCS>
 __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_partial_kernel(BwdArgs a) {
   constexpr int IB = Elem<DT>::bytes;
   constexpr int E = 16 / IB;
@@ -439,12 +444,12 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_partial_kernel(BwdArgs a) 
 #pragma unroll
     for (int k = 0; k < E; k++) acc[s][k] = 0.f;
   }
-  for (int64_t bb = b0; bb < b1; bb += DQ_DOCS) {
-    int64_t first[DQ_DOCS], len[DQ_DOCS];
-    float g[DQ_DOCS];
-    int j[DQ_DOCS][SLOTS];
+  for (int64_t bb = b0; bb < b1; bb += DOCS) {
+    int64_t first[DOCS], len[DOCS];
+    float g[DOCS];
+    int j[DOCS][SLOTS];
 #pragma unroll
-    for (int t = 0; t < DQ_DOCS; t++) {
+    for (int t = 0; t < DOCS; t++) {
       const int64_t b = bb + t;
       first[t] = 0;
       len[t] = 0;
@@ -459,7 +464,7 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dq_partial_kernel(BwdArgs a) 
     }
     // documents in order, so each chunk's sum has a fixed order
 #pragma unroll
-    for (int t = 0; t < DQ_DOCS; t++)
+    for (int t = 0; t < DOCS; t++)
 #pragma unroll
       for (int s = 0; s < SLOTS; s++) {
         if (j[t][s] >= 0 && j[t][s] < len[t]) {
