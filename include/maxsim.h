@@ -19,7 +19,8 @@
  *    default stream) and results are valid once that stream has synchronised.
  *  - Arguments are checked on the host before anything is enqueued; a failed
  *    check returns a negative maxsim_status and enqueues nothing. A call with
- *    n_docs == 0 returns MAXSIM_OK and enqueues nothing.
+ *    n_docs == 0 returns MAXSIM_OK and enqueues nothing (maxsim_backward with dQ
+ *    set, which writes zeros to dQ, is the one exception).
  *  - Contents are not checked: malformed doc_offsets (decreasing, or past the
  *    token array), NaN or Inf inputs give undefined scores.
  *  - Storage is row-major and densely packed. Q, D, codes and tables must be
@@ -133,7 +134,9 @@ int maxsim_score_argmax(const void *Q, int q_len, const void *D, const int64_t *
  *   grad_out   fp32 [n_docs]
  *   grad_dtype type of dQ and dD: MAXSIM_FP32, or dtype itself (each value rounded
  *              once, to nearest even, from its fp32 sum)
- *   dQ         nullable [q_len][d] in grad_dtype: written when set (needs the workspace)
+ *   dQ         nullable [q_len][d] in grad_dtype: written when set (needs the workspace);
+ *              with n_docs == 0 it is set to zero (the one launch a call with no
+ *              documents enqueues; D, tok_arg and grad_out may then be NULL)
  *   dD         nullable [tokens][d] in grad_dtype: every row of every document is
  *              written when set; rows of tokens outside all documents are left untouched
  *   workspace  device buffer of at least maxsim_backward_workspace_size(q_len, d,

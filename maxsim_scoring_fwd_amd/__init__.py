@@ -102,13 +102,58 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _out(out, n, device, dtype=torch.float32):
     if out is None:
         return torch.empty(n, dtype=dtype, device=device)
+    _need(out, "out", dtype, numel=n)
     return out
+
+
+# Host-side checks of dtypes and shapes. The library takes every type from its arguments
+# (the storage dtype from Q, offsets as int64, argmax as int32 ...) and cannot see a
+# tensor's dtype, so a mismatch here would make the kernels read past the end of a buffer.
+def _need(t, name: str, dtypes, shape=None, numel=None, dim=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not isinstance(dtypes, (tuple, list)):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(x) for x in dtypes)}, "
+                         f"got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
+_FLOAT_STORAGE = tuple(_TORCH_DTYPE)
+
+
+def _query(Q: torch.Tensor, dim: int = 2) -> None:
+    _need(Q, "Q", _FLOAT_STORAGE, dim=dim)
+
+
+def _docs_like(Q: torch.Tensor, D: torch.Tensor, doc_offsets) -> None:
+    """D shares Q's dtype and embedding dimension; [n_docs, nd, d] without offsets, else
+    [n_tokens, d] with int64 offsets [n_docs + 1]."""
+    _need(D, "D", Q.dtype, dim=2 if doc_offsets is not None else 3)
+    if D.shape[-1] != Q.shape[-1]:
+        raise ValueError(f"D has d = {D.shape[-1]}, Q has d = {Q.shape[-1]}")
+    if doc_offsets is not None:
+        _need(doc_offsets, "doc_offsets", torch.int64, dim=1)
+        if doc_offsets.numel() < 1:
+            raise ValueError("doc_offsets needs n_docs + 1 >= 1 entries")
 
 
 def maxsim_score(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor,
                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """CSR documents. Q [q_len, d], D [n_tokens, d] (same dtype), doc_offsets int64
     [n_docs+1]; returns fp32 scores [n_docs]."""
+    _query(Q)
+    if doc_offsets is None:
+        raise ValueError("maxsim_score needs doc_offsets (use maxsim_score_fixed without)")
+    _docs_like(Q, D, doc_offsets)
     n_docs = doc_offsets.numel() - 1
     out = _out(out, n_docs, Q.device)
     _check(lib().maxsim_score(_dev(Q, "Q"), Q.shape[0], _dev(D, "D"),
@@ -121,9 +166,10 @@ def maxsim_score_fixed(Q: torch.Tensor, D: torch.Tensor, doc_lens: torch.Tensor 
                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Fixed-length documents. Q [q_len, d], D [n_docs, nd, d]; doc_lens int32 [n_docs]
     (optional) masks trailing padding tokens. Returns fp32 scores [n_docs]."""
-    if D.dtype != Q.dtype:
-        raise ValueError("Q and D must share a dtype")
+    _query(Q)
+    _docs_like(Q, D, None)
     n_docs, nd = D.shape[0], D.shape[1]
+    _need(doc_lens, "doc_lens", torch.int32, numel=n_docs)
     out = _out(out, n_docs, Q.device)
     _check(lib().maxsim_score_fixed(_dev(Q, "Q"), Q.shape[0], _dev(D, "D"), n_docs, nd,
                                     _dev(doc_lens, "doc_lens"), Q.shape[1], _dtype_code(Q),
@@ -137,11 +183,18 @@ def maxsim_score_i8(Q: torch.Tensor, q_scale: torch.Tensor, D: torch.Tensor,
     """INT8 x INT8 with per-token fp32 scales. Fixed layout (D [n_docs, nd, d]) when
     doc_offsets is None, else CSR (D [n_tokens, d]). Returns scores, or (scores, tok_max,
     tok_arg) with with_token_max."""
+    _need(Q, "Q", torch.int8, dim=2)
     q_len, d = Q.shape
+    _need(q_scale, "q_scale", torch.float32, numel=q_len)
+    _need(D, "D", torch.int8, dim=2 if doc_offsets is not None else 3)
+    if D.shape[-1] != d:
+        raise ValueError(f"D has d = {D.shape[-1]}, Q has d = {d}")
     if doc_offsets is None:
         n_docs, nd = D.shape[0], D.shape[1]
     else:
+        _need(doc_offsets, "doc_offsets", torch.int64, dim=1)
         n_docs, nd = doc_offsets.numel() - 1, 0
+    _need(d_scale, "d_scale", torch.float32, numel=D.numel() // max(d, 1))
     out = _out(out, n_docs, Q.device)
     tm = ta = None
     if with_token_max:
@@ -166,11 +219,13 @@ def maxsim_score_argmax(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Ten
     """Scores with per-token maxima and argmax (lowest index on ties). Fixed layout
     (D [n_docs, nd, d]) when doc_offsets is None, else CSR (D [n_tokens, d]). Returns
     (scores fp32 [n_docs], tok_max fp32 [n_docs, q_len], tok_arg int32 [n_docs, q_len])."""
-    if D.dtype != Q.dtype:
-        raise ValueError("Q and D must share a dtype")
+    _query(Q)
+    _docs_like(Q, D, doc_offsets)
     q_len, d = Q.shape
     n_docs, nd = _docs(D, doc_offsets)
     out = _out(out, n_docs, Q.device)
+    _need(tok_max, "tok_max", torch.float32, shape=(n_docs, q_len))
+    _need(tok_arg, "tok_arg", torch.int32, shape=(n_docs, q_len))
     if tok_max is None:
         tok_max = torch.empty((n_docs, q_len), dtype=torch.float32, device=Q.device)
     if tok_arg is None:
@@ -188,12 +243,13 @@ def maxsim_score_batch(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tens
     """Several queries in one pass over the documents. Q [n_q, q_len, d]; fixed documents
     D [n_docs, nd, d] when doc_offsets is None, else CSR D [n_tokens, d]. Returns fp32 scores
     [n_q, n_docs]."""
-    if D.dtype != Q.dtype:
-        raise ValueError("Q and D must share a dtype")
+    _query(Q, dim=3)
+    _docs_like(Q, D, doc_offsets)
     n_q, q_len, d = Q.shape
     n_docs, nd = _docs(D, doc_offsets)
     if out is None:
         out = torch.empty((n_q, n_docs), dtype=torch.float32, device=Q.device)
+    _need(out, "out", torch.float32, numel=n_q * n_docs)
     _check(lib().maxsim_score_batch(_dev(Q, "Q"), n_q, q_len, _dev(D, "D"),
                                     _dev(doc_offsets, "doc_offsets"), n_docs, nd, d,
                                     _dtype_code(Q), _dev(out, "out"), _stream(stream)),
@@ -210,10 +266,14 @@ def maxsim_topk(scores: torch.Tensor, k: int, out_scores=None, out_index=None, w
                 stream=None):
     """The k best entries of each row of scores ([n] or [rows, n] fp32) by (score
     descending, index ascending). Returns (values, indices) shaped [k] or [rows, k]."""
-    if scores.dtype != torch.float32:
-        raise ValueError("scores must be float32")
+    _need(scores, "scores", torch.float32)
+    if scores.dim() not in (1, 2):
+        raise ValueError("scores must be [n] or [rows, n]")
     rows, n = (1, scores.shape[0]) if scores.dim() == 1 else scores.shape
     shape = (k,) if scores.dim() == 1 else (rows, k)
+    _need(out_scores, "out_scores", torch.float32, numel=rows * k)
+    _need(out_index, "out_index", torch.int32, numel=rows * k)
+    _need(workspace, "workspace", torch.uint8)
     if out_scores is None:
         out_scores = torch.empty(shape, dtype=torch.float32, device=scores.device)
     if out_index is None:
@@ -240,12 +300,17 @@ def maxsim_backward(Q: torch.Tensor, D: torch.Tensor, tok_arg: torch.Tensor,
     """Gradients of sum_b grad_out[b] * score_b from the forward argmax tok_arg. Returns
     (dQ [q_len, d], dD shaped like D), each None when not asked for; grad_dtype is float32
     or the dtype of Q and D."""
-    if D.dtype != Q.dtype:
-        raise ValueError("Q and D must share a dtype")
+    _query(Q)
+    _docs_like(Q, D, doc_offsets)
     if grad_dtype not in (torch.float32, Q.dtype):
         raise ValueError("grad_dtype must be float32 or the dtype of Q")
     q_len, d = Q.shape
     n_docs, nd = _docs(D, doc_offsets)
+    _need(tok_arg, "tok_arg", torch.int32, shape=(n_docs, q_len))
+    _need(grad_out, "grad_out", torch.float32, numel=n_docs)
+    _need(dQ, "dQ", grad_dtype, shape=(q_len, d))
+    _need(dD, "dD", grad_dtype, shape=tuple(D.shape))
+    _need(workspace, "workspace", torch.uint8)
     if want_dQ and dQ is None:
         dQ = torch.empty((q_len, d), dtype=grad_dtype, device=Q.device)
     if want_dD and dD is None:
@@ -297,9 +362,14 @@ def maxsim(Q: torch.Tensor, D: torch.Tensor, doc_offsets: torch.Tensor | None = 
 def maxsim_pq_tables(Q: torch.Tensor, C: torch.Tensor, T: torch.Tensor | None = None,
                      stream=None) -> torch.Tensor:
     """PQ distance tables T [q_len, M, K] fp32 from Q [q_len, M*dsub] and C [M, K, dsub] fp32."""
+    _query(Q)
+    _need(C, "C", torch.float32, dim=3)
     M, K, dsub = C.shape
+    if Q.shape[1] != M * dsub:
+        raise ValueError(f"Q has d = {Q.shape[1]}, the codebook M * dsub = {M * dsub}")
     if T is None:
         T = torch.empty((Q.shape[0], M, K), dtype=torch.float32, device=Q.device)
+    _need(T, "T", torch.float32, shape=(Q.shape[0], M, K))
     _check(lib().maxsim_pq_tables(_dev(Q, "Q"), Q.shape[0], _dtype_code(Q), _dev(C, "C"), M, K,
                                   dsub, _dev(T, "T"), _stream(stream)), "maxsim_pq_tables")
     return T
@@ -309,7 +379,15 @@ def maxsim_score_pq(T: torch.Tensor, codes: torch.Tensor, doc_offsets: torch.Ten
                     nd: int = 0, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Fused PQ lookup scoring. T [q_len, M, K] fp32, codes uint8 [n_tokens, M]; CSR when
     doc_offsets is given, else fixed documents of nd tokens."""
+    _need(T, "T", torch.float32, dim=3)
     q_len, M, K = T.shape
+    _need(codes, "codes", torch.uint8, dim=2)
+    if codes.shape[1] != M:
+        raise ValueError(f"codes have {codes.shape[1]} subspaces, T has M = {M}")
+    if doc_offsets is not None:
+        _need(doc_offsets, "doc_offsets", torch.int64, dim=1)
+    elif nd < 1:
+        raise ValueError("fixed documents need nd >= 1")
     n_docs = doc_offsets.numel() - 1 if doc_offsets is not None else codes.shape[0] // max(nd, 1)
     out = _out(out, n_docs, T.device)
     _check(lib().maxsim_score_pq(_dev(T, "T"), q_len, M, K, _dev(codes, "codes"),

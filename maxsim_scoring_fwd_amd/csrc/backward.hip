@@ -53,6 +53,7 @@ int launch_dd_lds(const BwdArgs &a, int seg_cap, int q_lds, const DeviceInfo &di
   BwdArgs ka = a;
   ka.doc_weight = doc_weight;
   ka.short_sets = short_sets;
+  log_launch(QLDS ? "bwd_dd<QLDS>" : "bwd_dd", (const void *)kern, grid, BWD_THREADS, lds, bpc);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(BWD_THREADS), lds, st, ka, seg_cap, q_lds);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
@@ -81,6 +82,17 @@ int launch_dq(const BwdArgs &a, hipStream_t st) {
   const unsigned rblocks = (unsigned)((n_elem + RED_ELEMS - 1) / RED_ELEMS);
   hipLaunchKernelGGL(bwd_dq_reduce_kernel<OT>, dim3(rblocks), dim3(BWD_THREADS), 0, st,
                      (const float *)a.partial, a.n_ranges, n_elem, a.dQ);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+// dQ = 0 in the gradient type: the range sum over no ranges stores 0 in every element.
+int zero_dq(void *dQ, int n_elem, int grad_dtype, hipStream_t st) {
+  const unsigned rblocks = (unsigned)((n_elem + RED_ELEMS - 1) / RED_ELEMS);
+  auto kern = grad_dtype == MAXSIM_FP32   ? bwd_dq_reduce_kernel<DT_FP32>
+              : grad_dtype == MAXSIM_BF16 ? bwd_dq_reduce_kernel<DT_BF16>
+                                          : bwd_dq_reduce_kernel<DT_FP16>;
+  hipLaunchKernelGGL(kern, dim3(rblocks), dim3(BWD_THREADS), 0, st, (const float *)nullptr, 0,
+                     n_elem, (char *)dQ);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
@@ -128,18 +140,22 @@ int maxsim_backward(const void *Q, int q_len, const void *D, const int64_t *doc_
   if (n_docs < 0 || q_len < 1 || q_len > MAXSIM_MAX_Q_LEN) return MAXSIM_ERR_SHAPE;
   if (d < MAXSIM_MIN_D || d > MAXSIM_MAX_D || d % 32 != 0) return MAXSIM_ERR_SHAPE;
   if (!doc_offsets && nd < 1) return MAXSIM_ERR_SHAPE;
-  if (!Q || !D || !tok_arg || !grad_out) return MAXSIM_ERR_NULL;
+  // with no documents, D, tok_arg and grad_out are empty and may be NULL
+  if (!Q || (n_docs > 0 && (!D || !tok_arg || !grad_out))) return MAXSIM_ERR_NULL;
   if (dQ && !workspace) return MAXSIM_ERR_NULL;
   if (!aligned(Q, 16) || !aligned(D, 16) || !aligned(tok_arg, 4) || !aligned(grad_out, 4) ||
       (doc_offsets && !aligned(doc_offsets, 8)) || (dQ && !aligned(dQ, 16)) ||
       (dD && !aligned(dD, 16)) || (workspace && !aligned(workspace, 16)))
     return MAXSIM_ERR_ALIGN;
-  if (n_docs == 0 || (!dQ && !dD)) return MAXSIM_OK;
+  if (!dQ && !dD) return MAXSIM_OK;
   if (dQ && workspace_bytes < maxsim_backward_workspace_size(q_len, d, n_docs))
     return MAXSIM_ERR_SHAPE;
+  if (n_docs == 0 && !dQ) return MAXSIM_OK;  // no rows of dD to write
   DeviceInfo di;
   int rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
+  // No documents: the loss is an empty sum and dQ is zero (dD has no rows).
+  if (n_docs == 0) return zero_dq(dQ, q_len * d, grad_dtype, (hipStream_t)stream);
   BwdArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs, doc_offsets ? 0 : nd, d,
             tok_arg, grad_out, (char *)dQ, (char *)dD, (float *)workspace,
             bwd_dq_ranges(q_len, d, n_docs)};

@@ -25,6 +25,10 @@ int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStre
   DenseArgs ka = a;
   ka.contiguous = contig >= 0 ? contig : !ARG && a.n_docs >= 4 * grid * DENSE_WAVES;
   if (a.offsets) ka.contiguous = 0;
+  char what[96];
+  std::snprintf(what, sizeof what, "dense<DT=%d,KSB=%d,QB=%d,P=%d,QLDS=%d,LM=%d,ARG=%d>", DT, KSB,
+                QB, P, (int)QLDS, LM, (int)ARG);
+  log_launch(what, (const void *)kern, grid, DENSE_THREADS, lds, bpc);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(DENSE_THREADS), lds, st, ka);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
@@ -55,7 +59,9 @@ int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipSt
     // CSR corpora: token-balanced ranges end on document boundaries, so a wave whose range
     // ends inside a long document finishes last, alone; a deeper ring shortens that tail
     // (measured depth 4 / 6 / 10 / 12: 80.5-80.7 / 80.7-81.0 / 81.2-81.4 / 81.8-81.9% of
-    // HBM peak on the lognormal corpus). 12 is the deepest ring at two waves per SIMD.
+    // HBM peak on the lognormal corpus). At depth 12 the kernel takes 253 VGPRs and 8 AGPRs,
+    // so it runs one wave per SIMD (one workgroup per CU): twelve tiles in flight per SIMD,
+    // as at depth 4 with three waves per SIMD, but from a single wave.
     if (a.offsets && depth == 0)
       return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
     if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -84,6 +85,22 @@ inline int env_knob(const char *name, int dflt) {
   const char *v = std::getenv(name);
   if (!v || !*v) return dflt;
   return std::atoi(v);
+}
+
+// MAXSIM_LOG_LAUNCH=1: one line on stderr per launch of the scoring kernels (variant, grid,
+// workgroup, LDS, resident workgroups per CU and the kernel's register counts), for checking
+// launch sizing against the hardware's limits.
+inline void log_launch(const char *what, const void *kernel, int64_t grid, int threads,
+                       size_t lds, int bpc) {
+  static const int on = env_knob("MAXSIM_LOG_LAUNCH", 0);
+  if (!on) return;
+  hipFuncAttributes fa{};
+  const bool ok = hipFuncGetAttributes(&fa, kernel) == hipSuccess;
+  std::fprintf(stderr,
+               "maxsim launch: %s grid=%lld threads=%d dyn_lds=%zu static_lds=%zu "
+               "blocks_per_cu=%d regs=%d max_threads=%d\n",
+               what, (long long)grid, threads, lds, ok ? (size_t)fa.sharedSizeBytes : (size_t)0,
+               bpc, ok ? fa.numRegs : -1, ok ? fa.maxThreadsPerBlock : -1);
 }
 
 }  // namespace maxsim

@@ -243,6 +243,7 @@ inline int pq_score_run(const PqScoreArgs &a, const DeviceInfo &di, hipStream_t 
   const int64_t max_wg = (int64_t)bpc * di.cus;
   int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
   if (grid < 1) grid = 1;
+  log_launch("pq_score", (const void *)pq_score_kernel, grid, PQ_THREADS, 0, bpc);
   hipLaunchKernelGGL(pq_score_kernel, dim3((unsigned)grid), dim3(PQ_THREADS), 0, st, a);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }

@@ -33,6 +33,10 @@ int launch_tiled(const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   const int64_t max_wg = (int64_t)bpc * di.cus;
   int64_t grid = a.n_docs < max_wg ? a.n_docs : max_wg;
   if (grid < 1) grid = 1;
+  char what[96];
+  std::snprintf(what, sizeof what, "tiled<DT=%d,KSB=%d,QBW=%d,ARG=%d,NW=%d,BATCH=%d>", DT, KSB,
+                QBW, (int)ARG, NW, (int)BATCH);
+  log_launch(what, (const void *)kern, grid, NW * WAVE, 0, bpc);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * WAVE), 0, st, a);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }

@@ -15,12 +15,45 @@ bool topk_args_ok(int64_t n, int rows, int k) {
          k <= TOPK_MAX_K;
 }
 
+// k <= 128: pass 1 leaves one sorted run per 2048 scores; merge passes reduce up to 64 runs
+// per workgroup until one run per row remains, whose first k entries are the result.
+// ws holds the runs of pass 1 and, when it takes two or more merge passes, of the first
+// merge pass; later passes alternate between the two regions.
+int topk_runs(const float *scores, int64_t n, int rows, int k, float *out_scores,
+              int32_t *out_index, uint64_t *ws, hipStream_t st) {
+  const int64_t c1 = (n + RUN_CHUNK - 1) / RUN_CHUNK;
+  uint64_t *buf[2] = {ws, ws ? ws + c1 * RUN * rows : nullptr};
+  TopkRunArgs a{scores, n, nullptr, 0, c1 > 1 ? buf[0] : nullptr, k, out_scores, out_index};
+  hipLaunchKernelGGL(topk_runs_kernel, dim3((unsigned)c1, (unsigned)rows), dim3(RUN_THREADS), 0,
+                     st, a);
+  if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
+  int64_t runs = c1;
+  for (int pass = 0; runs > 1; pass++) {
+    const int64_t groups = (runs + RUN_FANIN - 1) / RUN_FANIN;
+    a.in_runs = buf[pass & 1];
+    a.n_runs = runs;
+    a.out_runs = groups > 1 ? buf[(pass + 1) & 1] : nullptr;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)groups, (unsigned)rows),
+                       dim3(RUN_THREADS), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_LAUNCH;
+    runs = groups;
+  }
+  return MAXSIM_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t maxsim_topk_workspace_size(int64_t n, int rows, int k) {
   if (!topk_args_ok(n, rows, k)) return 0;
+  if (k <= RUN_MAX_K) {
+    // runs of the first pass, and of the second where more than one merge pass is needed
+    const int64_t c1 = (n + RUN_CHUNK - 1) / RUN_CHUNK;
+    if (c1 <= 1) return 0;
+    const int64_t c2 = (c1 + RUN_FANIN - 1) / RUN_FANIN;
+    return (size_t)(c1 + (c2 > 1 ? c2 : 0)) * RUN * (size_t)rows * sizeof(uint64_t);
+  }
   const int64_t c1 = chunks_of(n);
   if (c1 <= 1) return 0;
   const int64_t c2 = chunks_of(c1 * k);
@@ -41,9 +74,11 @@ int maxsim_topk(const float *scores, int64_t n, int rows, int k, float *out_scor
   int rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
+  if (k <= RUN_MAX_K) return topk_runs(scores, n, rows, k, out_scores, out_index,
+                                       (uint64_t *)workspace, st);
   const int64_t c1 = chunks_of(n);
   uint64_t *buf[2] = {(uint64_t *)workspace, (uint64_t *)workspace + (c1 > 1 ? c1 * k * rows : 0)};
-  TopkLevelArgs a{scores, nullptr, n, n, k, nullptr, 0, out_scores, out_index};
+  TopkLevelArgs a{scores, nullptr, n, n, k, nullptr, 0, out_scores, out_index, scores, n};
   for (int level = 0;; level++) {
     const int64_t chunks = chunks_of(a.count);
     if (chunks == 1) {  // the final chunk: sorted top-k out

@@ -6,17 +6,26 @@
 // of n fp32 scores, the k entries that come first in the order (score descending, index
 // ascending), in that order.
 //
-// Design for gfx950:
-//  * Each candidate is one 64-bit key: the score mapped to an unsigned integer whose order
-//    is the reverse of the float order (so a smaller key is a better score) in the high
-//    half, the document index in the low half. One unsigned comparison then implements the
-//    whole order, ties included, and the result is exact and the same on every run.
-//  * A workgroup of 1024 threads sorts a chunk of 2048 keys in LDS with a bitonic network
-//    and writes its first k. Chunks of a level run in parallel; each level divides the
-//    candidates by 2048 / k, until one chunk holds them all. No atomics anywhere.
-//  * Level 1 builds the keys straight from the score rows; later levels read the previous
-//    level's keys from a caller-provided workspace. Rows (queries of a batch) are
-//    independent: blockIdx.y is the row.
+// Every candidate is one 64-bit key: the score mapped to an unsigned integer whose order is
+// the reverse of the float order (a smaller key is a better score; -0 and +0 map to the same
+// key) in the high half, the document index in the low half. One unsigned comparison then
+// implements the whole order, ties included, so the result is exact and the same on every
+// run. The reported score is read back from the score row by index (its exact bits).
+//
+// k <= 128: sorted runs held by waves (bitonic top-k).
+//  * A run is 128 keys in ascending order held by one wave, two per lane (positions 2l and
+//    2l + 1 in lane l). A wave sorts its run with a bitonic network whose exchanges between
+//    lanes are register moves (DPP row and quad permutes, ds_swizzle, v_permlane32_swap):
+//    no LDS traffic and no barriers.
+//  * Two runs merge into the best 128 of their union: the elementwise minimum of one run and
+//    the other reversed is bitonic and holds those 128 keys; seven half-cleaner steps sort it.
+//  * Pass 1: a workgroup of 16 waves takes 2048 scores, each wave sorts 128 of them, and the
+//    16 runs merge in a tree through LDS (four barriers) into the chunk's best 128.
+//  * Later passes: a workgroup merges up to 64 runs (four per wave in turn, then the tree).
+//    The top-100 of 100K scores is one pass of 49 workgroups and one merge of 49 runs.
+// 128 < k <= 1024: a workgroup sorts 2048 keys in LDS (bitonic) and keeps k, level by level
+// until one chunk remains.
+// No atomics anywhere. Rows (queries of a batch) are independent: blockIdx.y is the row.
 #pragma once
 
 #include "device_common.hpp"
@@ -28,16 +37,12 @@ constexpr int TOPK_CHUNK = 2 * TOPK_THREADS;  // keys sorted per workgroup
 constexpr int TOPK_MAX_K = TOPK_THREADS;      // at most half a chunk survives a level
 
 // fp32 score -> unsigned key, smaller for better scores (-inf last; NaN is not ordered).
+// -0 and +0 compare equal as scores, so both get +0's key and the index decides.
 __device__ __forceinline__ uint32_t topk_score_key(float s) {
-  const uint32_t u = __float_as_uint(s);
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
   const uint32_t ascending = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~ascending;
-}
-
-__device__ __forceinline__ float topk_key_score(uint64_t key) {
-  const uint32_t ascending = ~(uint32_t)(key >> 32);
-  const uint32_t u = (ascending & 0x80000000u) ? (ascending & 0x7fffffffu) : ~ascending;
-  return __uint_as_float(u);
 }
 
 struct TopkLevelArgs {
@@ -50,6 +55,8 @@ struct TopkLevelArgs {
   int64_t out_stride;
   float *out_scores;        // final level: [rows][k]
   int32_t *out_index;       // final level: [rows][k]
+  const float *orig;        // the score rows [rows][n]: reported scores are read back by index
+  int64_t n;
 };
 
 __global__ void __launch_bounds__(TOPK_THREADS) topk_level_kernel(TopkLevelArgs a) {
@@ -101,10 +108,208 @@ __global__ void __launch_bounds__(TOPK_THREADS) topk_level_kernel(TopkLevelArgs 
       a.out_keys[row * a.out_stride + (int64_t)blockIdx.x * keep + e] = v;
     } else {
       const bool real = v != ~0ull;
-      a.out_scores[row * keep + e] = real ? topk_key_score(v) : -__builtin_inff();
-      a.out_index[row * keep + e] = real ? (int32_t)(uint32_t)v : -1;
+      const uint32_t idx = (uint32_t)v;
+      a.out_scores[row * keep + e] = real ? a.orig[row * a.n + idx] : -__builtin_inff();
+      a.out_index[row * keep + e] = real ? (int32_t)idx : -1;
     }
   }
+}
+
+
+// ---------------------------------------------------------------- k <= 128: sorted runs
+
+constexpr int RUN = 128;                      // keys per run: one wave, two per lane
+constexpr int RUN_WAVES = 16;
+constexpr int RUN_THREADS = RUN_WAVES * WAVE;
+constexpr int RUN_CHUNK = RUN_WAVES * RUN;    // scores per workgroup of the first pass
+constexpr int RUN_FANIN = 4 * RUN_WAVES;      // runs merged per workgroup of later passes
+constexpr int RUN_MAX_K = RUN;
+
+// The value of lane (lane ^ M), M < 64, as register moves: quad and row permutes (DPP) for
+// lane ^ 1, ^ 2, ^ 3, ^ 7, ^ 15, ds_swizzle (xor within 32 lanes) for the others below 32,
+// v_permlane32_swap for lane ^ 32, and the composition of the two above 32.
+template <int M> __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  static_assert(M > 0 && M < 64, "a lane of the wave");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 3) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
+  } else if constexpr (M == 7) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  } else if constexpr (M == 15) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, true);  // row_mirror
+  } else if constexpr (M < 32) {
+    // bitmask mode: lane' = ((lane & 0x1f) | 0) ^ M within each half of the wave
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (M << 10) | 0x1F);
+  } else if constexpr (M == 32) {
+    // with x in both operands, lanes 0..31 of the second result hold lanes 32..63 and
+    // lanes 32..63 of the first result hold lanes 0..31
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? p[0] : p[1];
+  } else {
+    return lane_xor<M ^ 32>(lane_xor<32>(x));
+  }
+}
+
+template <int M> __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  const uint32_t lo = lane_xor<M>((uint32_t)v), hi = lane_xor<M>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t kmin(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t kmax(uint64_t a, uint64_t b) { return a < b ? b : a; }
+
+// A run in a wave: k0 at position 2 * lane, k1 at 2 * lane + 1.
+struct Run {
+  uint64_t k0, k1;
+};
+
+// positions 2l and 2l + 1 (within the lane)
+__device__ __forceinline__ void run_cas1(Run &r) {
+  const uint64_t lo = kmin(r.k0, r.k1), hi = kmax(r.k0, r.k1);
+  r.k0 = lo;
+  r.k1 = hi;
+}
+
+// Half-cleaner step of stride 2M: position p against p ^ 2M (lane ^ M, the same slot); the
+// lower position keeps the smaller key.
+template <int M> __device__ __forceinline__ void run_xor(Run &r, int lane) {
+  const bool lower = (lane & M) == 0;
+  const uint64_t y0 = lane_xor64<M>(r.k0), y1 = lane_xor64<M>(r.k1);
+  r.k0 = lower ? kmin(r.k0, y0) : kmax(r.k0, y0);
+  r.k1 = lower ? kmin(r.k1, y1) : kmax(r.k1, y1);
+}
+
+// First step of a merge of size 2M + 2: position p against p ^ (2M + 1), its mirror within
+// the block (lane ^ M, the other slot); the lower position keeps the smaller key.
+template <int M> __device__ __forceinline__ void run_mirror(Run &r, int lane) {
+  const bool lower = (lane & ((M + 1) >> 1)) == 0;
+  const uint64_t y0 = lane_xor64<M>(r.k1), y1 = lane_xor64<M>(r.k0);
+  r.k0 = lower ? kmin(r.k0, y0) : kmax(r.k0, y0);
+  r.k1 = lower ? kmin(r.k1, y1) : kmax(r.k1, y1);
+}
+
+// Sort a bitonic run ascending: half-cleaners of strides 64, 32, ..., 1.
+__device__ __forceinline__ void run_clean(Run &r, int lane) {
+  run_xor<32>(r, lane);
+  run_xor<16>(r, lane);
+  run_xor<8>(r, lane);
+  run_xor<4>(r, lane);
+  run_xor<2>(r, lane);
+  run_xor<1>(r, lane);
+  run_cas1(r);
+}
+
+// Sort an arbitrary run ascending (bitonic sort in the mirror form: every merge sorts
+// ascending, so no element needs a direction).
+__device__ __forceinline__ void run_sort(Run &r, int lane) {
+  run_cas1(r);                                                      // blocks of 2
+  run_mirror<1>(r, lane);  run_cas1(r);                             // 4
+  run_mirror<3>(r, lane);  run_xor<1>(r, lane);  run_cas1(r);       // 8
+  run_mirror<7>(r, lane);  run_xor<2>(r, lane);  run_xor<1>(r, lane);  run_cas1(r);  // 16
+  run_mirror<15>(r, lane); run_xor<4>(r, lane);  run_xor<2>(r, lane);  run_xor<1>(r, lane);
+  run_cas1(r);                                                      // 32
+  run_mirror<31>(r, lane); run_xor<8>(r, lane);  run_xor<4>(r, lane);  run_xor<2>(r, lane);
+  run_xor<1>(r, lane);     run_cas1(r);                             // 64
+  run_mirror<63>(r, lane); run_xor<16>(r, lane); run_xor<8>(r, lane); run_xor<4>(r, lane);
+  run_xor<2>(r, lane);     run_xor<1>(r, lane);  run_cas1(r);       // 128
+}
+
+// r <- the best 128 keys of r and the sorted run at src (128 keys), sorted. Lane l reads
+// the pair at src[126 - 2l], src[127 - 2l]: the other run reversed.
+__device__ __forceinline__ void run_merge_from(Run &r, const uint64_t *src, int lane) {
+  const uint64_t b1 = src[126 - 2 * lane], b0 = src[127 - 2 * lane];
+  r.k0 = kmin(r.k0, b0);
+  r.k1 = kmin(r.k1, b1);
+  run_clean(r, lane);
+}
+
+__device__ __forceinline__ void run_store(const Run &r, uint64_t *dst, int lane) {
+  dst[2 * lane] = r.k0;
+  dst[2 * lane + 1] = r.k1;
+}
+
+struct TopkRunArgs {
+  const float *scores;      // [rows][n]
+  int64_t n;
+  const uint64_t *in_runs;  // merge passes: [rows][n_runs][RUN]
+  int64_t n_runs;           // runs per row at the input of a merge pass
+  uint64_t *out_runs;       // [rows][gridDim.x][RUN], or nullptr on the final pass
+  int k;
+  float *out_scores;        // final pass: [rows][k]
+  int32_t *out_index;       // final pass: [rows][k]
+};
+
+// The 16 runs of the workgroup merge into wave 0's run (a tree through LDS); then wave 0
+// writes either the row's top k or the workgroup's run.
+__device__ __forceinline__ void run_tree_and_emit(Run r, const TopkRunArgs &a, int64_t row,
+                                                  uint64_t (*lds)[RUN]) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x >> 6;
+  // At level `span`, wave w + span hands its run to wave w (w a multiple of 2 * span). The
+  // slots written at one level are never those read at an earlier one, so one barrier per
+  // level orders them.
+#pragma unroll
+  for (int span = 1; span < RUN_WAVES; span <<= 1) {
+    if ((w & (2 * span - 1)) == span) run_store(r, lds[w], lane);
+    __syncthreads();
+    if ((w & (2 * span - 1)) == 0) run_merge_from(r, lds[w + span], lane);
+  }
+  if (w != 0) return;
+  if (a.out_runs) {
+    run_store(r, a.out_runs + (row * gridDim.x + blockIdx.x) * RUN, lane);
+    return;
+  }
+  const uint64_t key[2] = {r.k0, r.k1};
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const int e = 2 * lane + h;
+    if (e < a.k) {
+      const bool real = key[h] != ~0ull;
+      const uint32_t idx = (uint32_t)key[h];
+      a.out_scores[row * a.k + e] = real ? a.scores[row * a.n + idx] : -__builtin_inff();
+      a.out_index[row * a.k + e] = real ? (int32_t)idx : -1;
+    }
+  }
+}
+
+// Pass 1: workgroup (chunk, row) takes scores [chunk * 2048, chunk * 2048 + 2048) of the row.
+__global__ void __launch_bounds__(RUN_THREADS) topk_runs_kernel(TopkRunArgs a) {
+  __shared__ uint64_t lds[RUN_WAVES][RUN];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.x * RUN_CHUNK + w * RUN + 2 * lane;
+  const float *src = a.scores + row * a.n;
+  Run r;
+  r.k0 = i0 < a.n ? ((uint64_t)topk_score_key(src[i0]) << 32) | (uint64_t)i0 : ~0ull;
+  r.k1 = i0 + 1 < a.n ? ((uint64_t)topk_score_key(src[i0 + 1]) << 32) | (uint64_t)(i0 + 1) : ~0ull;
+  run_sort(r, lane);
+  run_tree_and_emit(r, a, row, lds);
+}
+
+// Later passes: workgroup (group, row) merges runs [group * 64, group * 64 + 64) of the row;
+// wave w takes runs w, w + 16, w + 32, w + 48 in turn, then the tree.
+__global__ void __launch_bounds__(RUN_THREADS) topk_merge_kernel(TopkRunArgs a) {
+  __shared__ uint64_t lds[RUN_WAVES][RUN];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int w = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * RUN_FANIN + w;
+  const uint64_t *runs = a.in_runs + row * a.n_runs * RUN;
+  Run r{~0ull, ~0ull};
+  if (r0 < a.n_runs) {
+    r.k0 = runs[r0 * RUN + 2 * lane];
+    r.k1 = runs[r0 * RUN + 2 * lane + 1];
+  }
+#pragma unroll
+  for (int j = 1; j < RUN_FANIN / RUN_WAVES; j++) {
+    const int64_t rj = r0 + j * RUN_WAVES;
+    if (rj < a.n_runs) run_merge_from(r, runs + rj * RUN, lane);
+  }
+  run_tree_and_emit(r, a, row, lds);
 }
 
 }  // namespace maxsim

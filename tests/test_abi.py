@@ -198,7 +198,13 @@ def test_topk_argument_errors_and_workspace(L):
     assert f(S=P + 2) == ALIGN and f(ws=P + 4) == ALIGN
     w = L.maxsim_topk_workspace_size
     assert w(2048, 1, 100) == 0            # one chunk: no workspace
-    assert w(100000, 1, 100) == (49 + 3) * 100 * 8  # 49 chunks -> 4900 keys -> 3 chunks -> final
+    # k <= 128: one sorted run of 128 keys per 2048 scores; a second region when the runs
+    # need two or more merge passes (more than 64 runs)
+    assert w(100000, 1, 100) == 49 * 128 * 8
+    assert w(100000, 32, 10) == 49 * 128 * 8 * 32
+    assert w(5000000, 1, 128) == (2442 + 39) * 128 * 8
+    # k > 128: chunks of 2048 sorted in LDS, k kept per chunk, level by level
+    assert w(100000, 1, 129) == (49 + 4) * 129 * 8
     assert w(100000, 1, 1024) == (49 + 25) * 1024 * 8
     assert w(0, 1, 10) == 0 and w(10, 1, 0) == 0
 
@@ -221,7 +227,9 @@ def test_backward_argument_errors(L):
     assert bwd(L, wsb=1024) == SHAPE        # workspace too small
     assert bwd(L, dD=P + 8) == ALIGN
     assert bwd(L, ws=P + 4) == ALIGN
-    assert bwd(L, n=0) == OK
+    assert bwd(L, n=0, dQ=None) == OK       # no documents: no dD rows to write
+    assert bwd(L, n=0, dQ=None, D=None, ta=None, g=None) == OK  # empty arrays may be NULL
+    assert bwd(L, n=1, dQ=None, D=None) == NULL
     assert bwd(L, dQ=None, dD=None) == OK   # nothing asked for
 
 
@@ -238,6 +246,8 @@ def test_backward_workspace_size(L):
 def test_valid_call_without_gpu_reports_device_error(L):
     assert score(L) == DEVICE
     assert fixed(L) == DEVICE
+    # no documents but dQ set: dQ is zeroed on the device, so the device is needed
+    assert bwd(L, n=0) == DEVICE
 
 
 def test_python_binding_refuses_host_tensors(L):

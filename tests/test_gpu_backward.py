@@ -333,3 +333,28 @@ def test_autograd_function_matches_oracle():
     dQ, dD, mQ, mD = oracle_grads(c, ta, w)
     check_bound(Q.grad.float().cpu().numpy().astype(np.float64), dQ, mQ, 30, "bf16", "autograd dQ")
     check_bound(D.grad.float().cpu().numpy().astype(np.float64), dD, mD, 32, "bf16", "autograd dD")
+
+
+@pytest.mark.parametrize("grad_dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("layout", ["fixed", "csr"])
+def test_backward_no_documents_gives_zero_dQ(layout, grad_dtype):
+    """No documents: the loss is an empty sum, so dQ is exactly zero, even where its buffer
+    held garbage before the call (dD has no rows)."""
+    import torch
+    say(f"case: backward with no documents, {layout}, dQ in {grad_dtype}")
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[grad_dtype]
+    q_len, d = 32, 128
+    Q = torch.ones(q_len, d, dtype=torch.bfloat16, device="cuda")
+    if layout == "fixed":
+        D, off = torch.empty(0, 16, d, dtype=torch.bfloat16, device="cuda"), None
+    else:
+        D = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+        off = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ta = torch.empty(0, q_len, dtype=torch.int32, device="cuda")
+    g = torch.empty(0, dtype=torch.float32, device="cuda")
+    dQ = torch.full((q_len, d), 7.0, dtype=tdt, device="cuda")
+    dD = torch.empty(D.shape, dtype=tdt, device="cuda")
+    ms().maxsim_backward(Q, D, ta, g, off, grad_dtype=tdt, dQ=dQ, dD=dD)
+    torch.cuda.synchronize()
+    got = dQ.float().cpu().numpy()
+    assert np.all(got == 0.0) and not np.any(np.signbit(got))

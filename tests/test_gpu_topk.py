@@ -35,9 +35,14 @@ def scores_with_ties(seed, rows, n):
     return S
 
 
+# k <= 128 takes the run path (pass 1 over chunks of 2048, merges of up to 64 runs): 2048 and
+# 2049 scores are one and two chunks; 131072 / 131073 scores make 64 / 65 runs, one and two
+# merge passes; 5M scores make 2442 runs, two merge passes. k > 128 takes the LDS levels.
 @pytest.mark.parametrize("n,k", [(1, 1), (5, 3), (100, 100), (2047, 10), (2048, 1024), (2049, 1024),
                                  (100_000, 10), (100_000, 100), (100_000, 1024), (1_000_000, 100),
-                                 (5_000_000, 1000), (30, 64)])
+                                 (5_000_000, 1000), (30, 64), (2048, 128), (2049, 128),
+                                 (131_072, 128), (131_073, 100), (5_000_000, 100), (100_000, 129),
+                                 (4096, 1), (300, 128)])
 def test_topk_exact(n, k):
     say(f"case: top-{k} of {n}")
     S = scores_with_ties(800 + n % 997 + k, 1, n)[0]
@@ -47,7 +52,8 @@ def test_topk_exact(n, k):
     assert np.array_equal(v.view(np.uint32), wv[0].view(np.uint32))
 
 
-@pytest.mark.parametrize("rows,n,k", [(3, 5000, 50), (32, 100_000, 100), (7, 2048, 1)])
+@pytest.mark.parametrize("rows,n,k", [(3, 5000, 50), (32, 100_000, 100), (7, 2048, 1),
+                                      (5, 200_000, 128), (4, 3000, 200)])
 def test_topk_rows(rows, n, k):
     say(f"case: top-{k} of {rows} rows x {n}")
     S = scores_with_ties(850 + rows, rows, n)
@@ -75,3 +81,21 @@ def test_topk_after_scoring_planted_documents():
     assert set(i[:10].tolist()) == set(c.planted.tolist())
     assert np.array_equal(i, oracle.topk(got, 100)[1][0])  # exact on the GPU's own scores
     topk_agree(got.astype(np.float64), want, 100, tie=2 * TOL)
+
+
+@pytest.mark.parametrize("k", [100, 300])
+def test_topk_signed_zeros_tie_by_index(k):
+    """-0.0 and +0.0 are equal scores: their order is the index order whatever the sign, and
+    the reported values keep each entry's own bits."""
+    say(f"case: top-{k} with signed zeros")
+    rng = np.random.default_rng(870 + k)
+    n = 5000
+    S = np.where(rng.random(n) < 0.5, -1.0, 1.0).astype(np.float32) * 0.0  # +-0 only
+    S[rng.random(n) < 0.01] = np.float32(0.5)
+    S[7], S[9] = np.float32(-0.0), np.float32(0.0)  # -0 at the lower index of a pair
+    v, i = gpu_topk(S, k)
+    wv, wi = oracle.topk(S, k)
+    assert np.array_equal(i, wi[0]), np.flatnonzero(i != wi[0])[:5]
+    assert np.array_equal(v.view(np.uint32), wv[0].view(np.uint32))
+    pos7, pos9 = int(np.flatnonzero(i == 7)[0]), int(np.flatnonzero(i == 9)[0])
+    assert pos7 < pos9 and np.signbit(v[pos7]) and not np.signbit(v[pos9])
