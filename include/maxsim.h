@@ -53,7 +53,8 @@ enum maxsim_status {
   MAXSIM_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
   MAXSIM_ERR_UNSUPPORTED = -5, /* valid, but no kernel for this combination */
   MAXSIM_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
-  MAXSIM_ERR_DEVICE = -7       /* no usable gfx950 device is current */
+  MAXSIM_ERR_DEVICE = -7,      /* no usable gfx950 device is current */
+  MAXSIM_ERR_SCRATCH = -8      /* needs more than the library's static scratch memory */
 };
 
 /* Limits checked by every entry point. */
@@ -211,6 +212,25 @@ int maxsim_topk(const float *scores, int64_t n, int rows, int k, float *out_scor
 
 /* Workspace bytes maxsim_topk needs (0 when n fits one 2048-entry chunk or on bad sizes). */
 size_t maxsim_topk_workspace_size(int64_t n, int rows, int k);
+
+/*
+ * maxsim_topk for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same selection and
+ * the same results, with the workspace taken from a static device array inside the
+ * library (maxsim_topk_scratch_bytes(), 8 MiB; each GPU the library runs on holds its own
+ * copy until the process ends). Allocates nothing.
+ *   Arguments as for maxsim_topk, without the workspace.
+ *   Returns MAXSIM_ERR_SCRATCH when maxsim_topk_workspace_size(n, rows, k) exceeds the
+ *   static array (for k <= 128: rows * (runs of 2048 scores + runs of the first merge) of
+ *   1 KiB each, 8192 in all).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and give undefined results.
+ */
+int maxsim_topk_no_alloc(const float *scores, int64_t n, int rows, int k, float *out_scores,
+                         int32_t *out_index, void *stream);
+
+/* Bytes of the static scratch array maxsim_topk_no_alloc uses on each GPU. */
+size_t maxsim_topk_scratch_bytes(void);
 
 /* Static description of a status code. */
 const char *maxsim_status_string(int status);

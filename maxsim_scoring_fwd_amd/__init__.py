@@ -24,7 +24,7 @@ _TORCH_DTYPE = {torch.bfloat16: MAXSIM_BF16, torch.float16: MAXSIM_FP16,
 
 STATUS = {0: "MAXSIM_OK", -1: "MAXSIM_ERR_NULL", -2: "MAXSIM_ERR_SHAPE", -3: "MAXSIM_ERR_DTYPE",
           -4: "MAXSIM_ERR_ALIGN", -5: "MAXSIM_ERR_UNSUPPORTED", -6: "MAXSIM_ERR_LAUNCH",
-          -7: "MAXSIM_ERR_DEVICE"}
+          -7: "MAXSIM_ERR_DEVICE", -8: "MAXSIM_ERR_SCRATCH"}
 
 
 class MaxSimError(RuntimeError):
@@ -59,12 +59,15 @@ def lib() -> ctypes.CDLL:
         L.maxsim_topk.argtypes = [vp, i64, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.maxsim_topk_workspace_size.argtypes = [i64, i32, i32]
         L.maxsim_topk_workspace_size.restype = ctypes.c_size_t
+        L.maxsim_topk_no_alloc.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.maxsim_topk_scratch_bytes.argtypes = []
+        L.maxsim_topk_scratch_bytes.restype = ctypes.c_size_t
         L.maxsim_status_string.argtypes = [i32]
         L.maxsim_status_string.restype = ctypes.c_char_p
         L.maxsim_version.argtypes = []
         for f in ("maxsim_score", "maxsim_score_fixed", "maxsim_score_i8", "maxsim_pq_tables",
                   "maxsim_score_pq", "maxsim_version", "maxsim_score_argmax", "maxsim_backward",
-                  "maxsim_score_batch", "maxsim_topk"):
+                  "maxsim_score_batch", "maxsim_topk", "maxsim_topk_no_alloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib_handle = L
     return _lib_handle
@@ -286,6 +289,27 @@ def maxsim_topk(scores: torch.Tensor, k: int, out_scores=None, out_index=None, w
                              _dev(out_index, "out_index"), _dev(workspace, "workspace"), ws_bytes,
                              _stream(stream)), "maxsim_topk")
     return out_scores, out_index
+
+
+def maxsim_topk_no_alloc(scores: torch.Tensor, k: int, out_scores: torch.Tensor,
+                         out_index: torch.Tensor, stream=None):
+    """maxsim_topk with the library's static scratch memory instead of a workspace: the
+    library allocates nothing (outputs are the caller's). Calls overlapping on one GPU race."""
+    _need(scores, "scores", torch.float32)
+    if scores.dim() not in (1, 2):
+        raise ValueError("scores must be [n] or [rows, n]")
+    rows, n = (1, scores.shape[0]) if scores.dim() == 1 else scores.shape
+    _need(out_scores, "out_scores", torch.float32, numel=rows * k)
+    _need(out_index, "out_index", torch.int32, numel=rows * k)
+    _check(lib().maxsim_topk_no_alloc(_dev(scores, "scores"), n, rows, k,
+                                      _dev(out_scores, "out_scores"), _dev(out_index, "out_index"),
+                                      _stream(stream)), "maxsim_topk_no_alloc")
+    return out_scores, out_index
+
+
+def topk_scratch_bytes() -> int:
+    """Bytes of the static scratch array maxsim_topk_no_alloc uses on each GPU."""
+    return int(lib().maxsim_topk_scratch_bytes())
 
 
 def backward_workspace_size(q_len: int, d: int, n_docs: int) -> int:

@@ -189,6 +189,7 @@ const char *maxsim_status_string(int status) {
   case MAXSIM_ERR_UNSUPPORTED: return "no kernel for this combination of sizes";
   case MAXSIM_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
   case MAXSIM_ERR_DEVICE: return "no gfx950 device is current";
+  case MAXSIM_ERR_SCRATCH: return "the call needs more than the library's static scratch memory";
   }
   return "unknown status";
 }

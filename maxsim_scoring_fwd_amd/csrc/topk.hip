@@ -1,12 +1,40 @@
 // libmaxsim top-k entry points (include/maxsim.h): the best k documents of each score row.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "host_common.hpp"
 #include "topk_kernel.hpp"
 
 using namespace maxsim;
 
+// Scratch memory of maxsim_topk_no_alloc: the sorted runs (or kept keys) between passes.
+// Each GPU the library runs on holds its own copy until the process ends. Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the symbol): it uses
+// the device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t TOPK_SCRATCH_BYTES = size_t(8) << 20;
+static __device__ __align__(256) uint64_t scratch[TOPK_SCRATCH_BYTES / sizeof(uint64_t)];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void **ptr) {
+  static std::mutex mu;
+  static std::unordered_map<int, void *> addr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MAXSIM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MAXSIM_ERR_DEVICE;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return MAXSIM_OK;
+}
 
 int64_t chunks_of(int64_t count) { return (count + TOPK_CHUNK - 1) / TOPK_CHUNK; }
 
@@ -97,5 +125,21 @@ int maxsim_topk(const float *scores, int64_t n, int rows, int k, float *out_scor
     a.in_stride = a.out_stride;
   }
 }
+
+int maxsim_topk_no_alloc(const float *scores, int64_t n, int rows, int k, float *out_scores,
+                         int32_t *out_index, void *stream) {
+  if (!topk_args_ok(n, rows, k)) return MAXSIM_ERR_SHAPE;
+  if (maxsim_topk_workspace_size(n, rows, k) > TOPK_SCRATCH_BYTES) return MAXSIM_ERR_SCRATCH;
+  if (!scores || !out_scores || !out_index) return MAXSIM_ERR_NULL;
+  DeviceInfo di;
+  int rc = current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  void *ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != MAXSIM_OK) return rc;
+  return maxsim_topk(scores, n, rows, k, out_scores, out_index, ws, TOPK_SCRATCH_BYTES, stream);
+}
+
+size_t maxsim_topk_scratch_bytes(void) { return TOPK_SCRATCH_BYTES; }
 
 }  // extern "C"
