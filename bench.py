@@ -148,6 +148,20 @@ def _fill_rows(dst, seed, row0_of, nrows_total, d, dtype, device, chunk_rows, sc
                                        dtype, device)
 
 
+def pq_codes(seed, n_tokens, C):
+    """PQ codes of a corpus: the nearest-centroid codes of its generated unit-norm tokens
+    (the document stream of the seed), encoded in chunks."""
+    import numpy as np
+
+    import gen
+    out = np.empty((n_tokens, C.shape[0]), dtype=np.uint8)
+    step = 1 << 20
+    for r0 in range(0, n_tokens, step):
+        r1 = min(n_tokens, r0 + step)
+        out[r0:r1] = gen.encoded_codes(seed, gen.S_DOCS, r0, r1 - r0, C)
+    return out
+
+
 def make_inputs(w, device):
     """Generate the workload on the host in chunks and copy it to the device. With a pool,
     the first `pool` documents are generated and repeated (device copies) to fill B."""
@@ -178,7 +192,7 @@ def make_inputs(w, device):
         if w["path"] == "pq":
             C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
             inp["C"] = torch.from_numpy(C).to(device)
-            inp["codes"] = torch.from_numpy(gen.codes(seed, n_tok, PQ_M, PQ_K)).to(device)
+            inp["codes"] = torch.from_numpy(pq_codes(seed, n_tok, C)).to(device)
             inp["T"] = torch.empty((w["q_len"], PQ_M, PQ_K), dtype=torch.float32, device=device)
             return inp
         D = torch.empty((B * nd, d), dtype=tdt, device=device)
@@ -203,7 +217,7 @@ def make_inputs(w, device):
     if w["path"] == "pq":
         C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
         inp["C"] = torch.from_numpy(C).to(device)
-        inp["codes"] = torch.from_numpy(gen.codes(seed, T, PQ_M, PQ_K)).to(device)
+        inp["codes"] = torch.from_numpy(pq_codes(seed, T, C)).to(device)
         inp["T"] = torch.empty((w["q_len"], PQ_M, PQ_K), dtype=torch.float32, device=device)
         return inp
     D = torch.empty((T, d), dtype=tdt, device=device)
@@ -345,7 +359,9 @@ def cpu_baseline(w, budget_s: float):
 
     import gen
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    # every host core the process may use (its CPU affinity; OMP_NUM_THREADS where the
+    # environment sets a smaller share)
+    threads = oracle.host_threads()
     seed, d, dt, q = w["seed"], w["d"], w["dtype"], w["q_len"]
 
     def score(n):
@@ -358,7 +374,7 @@ def cpu_baseline(w, budget_s: float):
         if w["path"] == "pq":
             Qh = gen.tokens(seed, gen.S_QUERY, 0, q, d, dt)
             C = gen.codebook(seed, PQ_M, PQ_K, PQ_DSUB)
-            codes = gen.codes(seed, n_tok, PQ_M, PQ_K)
+            codes = pq_codes(seed, n_tok, C)
             t = time.perf_counter()
             T = oracle.pq_tables(Qh, dt, C)
             oracle.maxsim_pq(T, codes, offsets=off, nd=w.get("nd", 0), nthreads=threads)
@@ -408,7 +424,60 @@ def cpu_baseline(w, budget_s: float):
     return {"value": round(n_q * n / t, 1), "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"first {n} of the {w['B']} documents of the same workload "
                       f"(float64 oracle, {t:.1f} s)",
-            "cpu_model": model, "host_cpus_visible": os.cpu_count()}
+            "cpu_model": model, "host_cpus_visible": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+# Vector instructions per similarity in the query-tiled kernels' inner loops: INT8 a
+# convert, the product with its scale product (the scale products themselves run on the
+# matrix core) and half a three-way max; bf16 / fp16 half a three-way max.
+VALU_PER_SIMILARITY = {"i8": 2.5, "bf16": 0.5, "fp16": 0.5}
+# matrix-core cycles per 16 x 16 tile and query block relative to the dot products alone:
+# INT8 adds a 32-cycle 16x16x1 4-block fp32 MFMA (scale products) per four 16-cycle int8
+# ones at d = 128
+MFMA_EXTRA = {"i8": 1.25, "bf16": 1.0, "fp16": 1.0}
+
+
+def compute_ceilings(ms, w, achieved, stream, median_ms):
+    """Measured ceilings of a matrix-core-bound workload, at the query-tiled kernels'
+    occupancy (two waves per SIMD): the sustained MFMA rate of its dtype, the sustained
+    vector-ALU rate, and the additive bound of the two (on MI355X the matrix core and the
+    vector unit of a SIMD measure as taking turns, not overlapping: maxsim_calib_mix)."""
+    import torch
+    sink = torch.zeros(65536, dtype=torch.float32, device="cuda")
+    kind = 2 if w["dtype"] == "i8" else 0
+    mfma_ops = ms.calib_mfma(kind, 4000, 2, sink)
+    mfma = mfma_ops / (median_ms(lambda: ms.calib_mfma(kind, 4000, 2, sink)) * 1e-3) / 1e12
+    valu_ops = ms.calib_valu(20000, 2, sink)
+    valu = valu_ops / (median_ms(lambda: ms.calib_valu(20000, 2, sink)) * 1e-3) / 1e12
+    # one VALU instruction per lane per FMA (2 FLOP): lane-instructions per second
+    lane_instr = valu * 1e12 / 2
+    ops_per_sim = 2 * w["d"]
+    valu_bound = lane_instr / VALU_PER_SIMILARITY[w["dtype"]] * ops_per_sim / 1e12
+    mfma_bound = mfma / MFMA_EXTRA[w["dtype"]]
+    additive = 1.0 / (1.0 / mfma_bound + 1.0 / valu_bound)
+    return {"mfma_sustained_TOPs_2w": round(mfma, 1),
+            "frac_of_mfma_sustained": round(achieved / mfma, 4),
+            "valu_fp32_TFLOPs_2w": round(valu, 1),
+            "valu_per_similarity": VALU_PER_SIMILARITY[w["dtype"]],
+            "valu_bound_TOPs": round(valu_bound, 1),
+            "mfma_plus_valu_bound_TOPs": round(additive, 1),
+            "frac_of_mfma_plus_valu_bound": round(achieved / additive, 4)}
+
+
+def lds_ceilings(ms, achieved, median_ms):
+    """Measured LDS read rates: contiguous 128-bit reads, and the PQ lookup pattern (16-byte
+    reads of random table rows) that bounds the PQ scoring kernel."""
+    import torch
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    out = {}
+    for pat, name in ((0, "contiguous"), (1, "pq_pattern")):
+        b = ms.calib_lds(pat, 2000, sink)
+        out[f"lds_read_GBps_{name}"] = round(b / (median_ms(lambda: ms.calib_lds(pat, 2000, sink))
+                                                  * 1e-3) / 1e9, 1)
+    out["frac_of_lds_pq_pattern"] = round(achieved / out["lds_read_GBps_pq_pattern"], 4)
+    return out
 
 
 def copy_probe(mib: int, steps: int):
@@ -568,6 +637,10 @@ def main():
             context["stream_read_same_bytes_GBps"] = round(small_gbs, 1)
             context["frac_of_stream_read_same_bytes"] = round(achieved / small_gbs, 4)
             log(f"stream read of the same {n_small * 4} bytes, caches flushed: {small_gbs:.0f} GB/s")
+        if bound == "mfma" and w["dtype"] != "fp32":
+            context.update(compute_ceilings(ms, w, achieved, stream, median_ms))
+        if bound == "lds":
+            context.update(lds_ceilings(ms, achieved, median_ms))
         if w["path"] == "train":
             # the dD kernel mostly writes: its ceiling is the streaming-write rate
             wr_gbs = buf.numel() * 4 / (median_ms(lambda: ms.calib_write(buf)) * 1e-3) / 1e9

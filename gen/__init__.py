@@ -35,7 +35,7 @@ def build(force: bool = True) -> str:
     """Compile the generator shared library in place (gcc, no GPU code)."""
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
                                "-o", tmp, _SRC, "-lm", "-lpthread"])
         os.replace(tmp, _SO)
     return _SO
@@ -65,6 +65,7 @@ def _lib():
         lib.gen_codebook.argtypes = [u64, u64, i32, i32, i32, vp]
         lib.gen_codes.argtypes = [u64, u64, i64, i64, i32, i32, vp]
         lib.gen_pq_encode.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+        lib.gen_encoded_codes.argtypes = [u64, u64, i64, i64, i32, i32, i32, vp, vp, i32]
         lib.gen_round_f32_to_bf16.argtypes = [vp, i64, vp]
         lib.gen_round_f32_to_f16.argtypes = [vp, i64, vp]
         _lib_cache = lib
@@ -76,7 +77,16 @@ def _ptr(a: np.ndarray | None):
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Host cores this process may run on (its CPU affinity), or OMP_NUM_THREADS where the
+    environment sets a smaller share."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def _check(rc: int, what: str):
@@ -290,6 +300,18 @@ def pq_encode(x: np.ndarray, C: np.ndarray) -> np.ndarray:
     out = np.empty((x.shape[0], M), dtype=np.uint8)
     _check(_lib().gen_pq_encode(_ptr(x), x.shape[0], M, K, dsub, _ptr(C), _ptr(out)),
            "gen_pq_encode")
+    return out
+
+
+def encoded_codes(seed: int, stream: int, row0: int, n: int, C: np.ndarray,
+                  nthreads: int | None = None) -> np.ndarray:
+    """Nearest-centroid PQ codes [n, M] of token rows [row0, row0 + n) of a stream, each
+    generated in double and encoded as pq_encode does, without holding the vectors."""
+    M, K, dsub = C.shape
+    C = np.ascontiguousarray(C, dtype=np.float32)
+    out = np.empty((n, M), dtype=np.uint8)
+    _check(_lib().gen_encoded_codes(seed, stream, row0, n, M, K, dsub, _ptr(C), _ptr(out),
+                                    nthreads or default_threads()), "gen_encoded_codes")
     return out
 
 

@@ -321,6 +321,84 @@ int gen_pq_encode(const double *x, int64_t n, int M, int K, int dsub, const floa
   return 0;
 }
 
+/*
+ * Rows [row0, row0 + n) of a unit-norm Gaussian token stream (d = M * dsub), each
+ * generated in double and encoded as gen_pq_encode does (nearest centroid of each
+ * sub-vector, ties to the lowest k), over nthreads threads: PQ codes of a corpus
+ * without holding its vectors.
+ */
+typedef struct {
+  uint64_t seed, stream;
+  int64_t row0, r_begin, r_end;
+  int M, K, dsub;
+  const float *C;
+  uint8_t *codes;
+} enc_job;
+
+/* The same distances and choice as gen_pq_encode, laid out so that the loop over the
+ * centroids is innermost (each centroid's sum still runs over t in increasing order). */
+static void *enc_worker(void *arg) {
+  enc_job *j = (enc_job *)arg;
+  const int M = j->M, K = j->K, dsub = j->dsub, d = M * dsub;
+  double *x = (double *)malloc(sizeof(double) * (size_t)d);
+  double *dist = (double *)malloc(sizeof(double) * (size_t)K);
+  double *ct = (double *)malloc(sizeof(double) * (size_t)M * dsub * K);  /* [m][t][k] */
+  for (int m = 0; m < M; m++)
+    for (int t = 0; t < dsub; t++)
+      for (int k = 0; k < K; k++)
+        ct[((size_t)m * dsub + t) * K + k] = (double)j->C[((size_t)m * K + k) * dsub + t];
+  for (int64_t r = j->r_begin; r < j->r_end; r++) {
+    gen_unit_token(j->seed, j->stream, j->row0 + r, d, x);
+    for (int m = 0; m < M; m++) {
+      for (int k = 0; k < K; k++) dist[k] = 0.0;
+      for (int t = 0; t < dsub; t++) {
+        const double xt = x[m * dsub + t];
+        const double *c = ct + ((size_t)m * dsub + t) * K;
+        for (int k = 0; k < K; k++) dist[k] += (xt - c[k]) * (xt - c[k]);
+      }
+      double best = INFINITY;
+      int arg = 0;
+      for (int k = 0; k < K; k++)
+        if (dist[k] < best) {
+          best = dist[k];
+          arg = k;
+        }
+      j->codes[r * M + m] = (uint8_t)arg;
+    }
+  }
+  free(ct);
+  free(dist);
+  free(x);
+  return NULL;
+}
+
+int gen_encoded_codes(uint64_t seed, uint64_t stream, int64_t row0, int64_t n, int M, int K,
+                      int dsub, const float *C, uint8_t *codes, int nthreads) {
+  if (n < 0 || M < 1 || K < 1 || K > 256 || dsub < 1 || !C || !codes) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if ((int64_t)nthreads > n / 64 + 1) nthreads = (int)(n / 64 + 1);
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  enc_job jobs[256];
+  for (int t = 0; t < nthreads; t++) {
+    enc_job *j = &jobs[t];
+    j->seed = seed;
+    j->stream = stream;
+    j->row0 = row0;
+    j->r_begin = n * t / nthreads;
+    j->r_end = n * (t + 1) / nthreads;
+    j->M = M;
+    j->K = K;
+    j->dsub = dsub;
+    j->C = C;
+    j->codes = codes;
+    if (t > 0) pthread_create(&th[t], NULL, enc_worker, j);
+  }
+  enc_worker(&jobs[0]);
+  for (int t = 1; t < nthreads; t++) pthread_join(th[t], NULL);
+  return 0;
+}
+
 /* Storage rounding exposed for tests of the encoders. */
 void gen_round_f32_to_bf16(const float *x, int64_t n, uint16_t *out) {
   for (int64_t i = 0; i < n; i++) out[i] = f32_to_bf16_rne(x[i]);

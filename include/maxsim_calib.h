@@ -41,6 +41,31 @@ int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
 int maxsim_calib_mfma(int kind, int iters, int waves_per_simd, float *sink, double *ops,
                       void *stream);
 
+/*
+ * Vector-ALU throughput: 8 independent chains of fp32 fused multiply-adds per lane (one
+ * non-packed VALU instruction each), waves_per_simd x 4 x CUs waves of `iters` rounds.
+ * *ops receives the FLOP count (2 per lane and FMA).
+ */
+int maxsim_calib_valu(int iters, int waves_per_simd, float *sink, double *ops, void *stream);
+
+/*
+ * Matrix core and vector ALU side by side: per round 8 independent 16x16x64 int8 MFMA
+ * chains and valu_per_mfma (0, 1, 2, 4 or 8) x 8 independent fp32 FMAs, with no data
+ * flowing between them. Timed against valu_per_mfma = 0 and against maxsim_calib_valu it
+ * shows how far the two units overlap. *ops receives the int8 MFMA integer-op count.
+ */
+int maxsim_calib_mix(int valu_per_mfma, int iters, int waves_per_simd, float *sink,
+                     double *ops, void *stream);
+
+/*
+ * LDS read rate: one 1024-thread workgroup per CU with 128 KiB of LDS, every lane issuing
+ * 16 x iters 16-byte reads. pattern 0: each wave reads 1 KiB of contiguous LDS per
+ * instruction (conflict-free); pattern 1: the PQ lookup pattern (lane pairs share a token
+ * and read the two halves of row (m, code) of a [16][256][8] fp32 table, codes random).
+ * *bytes receives the LDS bytes read. sink: >= 65536 words, not written in practice.
+ */
+int maxsim_calib_lds(int pattern, int iters, uint32_t *sink, double *bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -438,6 +438,12 @@ def _calib_lib():
         L.maxsim_calib_read.restype = ctypes.c_int
         L.maxsim_calib_copy.restype = ctypes.c_int
         L.maxsim_calib_mfma.restype = ctypes.c_int
+        L.maxsim_calib_valu.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.maxsim_calib_valu.restype = ctypes.c_int
+        L.maxsim_calib_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.maxsim_calib_mix.restype = ctypes.c_int
+        L.maxsim_calib_lds.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        L.maxsim_calib_lds.restype = ctypes.c_int
         L._calib_bound = True
     return L
 
@@ -469,3 +475,29 @@ def calib_mfma(kind: int, iters: int, waves_per_simd: int, sink: torch.Tensor, s
                                           ctypes.addressof(ops), _stream(stream)),
            "maxsim_calib_mfma")
     return ops.value
+
+
+def calib_valu(iters: int, waves_per_simd: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch independent fp32 FMA chains; returns the FLOP count of the launch."""
+    ops = ctypes.c_double(0.0)
+    _check(_calib_lib().maxsim_calib_valu(iters, waves_per_simd, _dev(sink, "sink"),
+                                          ctypes.addressof(ops), _stream(stream)), "maxsim_calib_valu")
+    return ops.value
+
+
+def calib_mix(valu_per_mfma: int, iters: int, waves_per_simd: int, sink: torch.Tensor,
+              stream=None) -> float:
+    """Launch int8 MFMA chains with valu_per_mfma independent FMAs per MFMA; returns the
+    int8 integer-op count of the launch."""
+    ops = ctypes.c_double(0.0)
+    _check(_calib_lib().maxsim_calib_mix(valu_per_mfma, iters, waves_per_simd, _dev(sink, "sink"),
+                                         ctypes.addressof(ops), _stream(stream)), "maxsim_calib_mix")
+    return ops.value
+
+
+def calib_lds(pattern: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the LDS read-rate kernel (0: contiguous, 1: PQ lookups); returns LDS bytes read."""
+    b = ctypes.c_double(0.0)
+    _check(_calib_lib().maxsim_calib_lds(pattern, iters, _dev(sink, "sink"), ctypes.addressof(b),
+                                         _stream(stream)), "maxsim_calib_lds")
+    return b.value

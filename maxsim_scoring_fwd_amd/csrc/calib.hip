@@ -206,3 +206,155 @@ extern "C" int maxsim_calib_mfma(int kind, int iters, int waves_per_simd, float 
   }
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
+
+// ---- vector-ALU throughput, matrix core + vector ALU together, LDS read rate ----
+
+namespace {
+
+constexpr int VA_CHAINS = 8;
+
+// VALU: 8 independent chains of fp32 fused multiply-adds per lane (one VALU instruction
+// each, never packed), `iters` rounds.
+__global__ void __launch_bounds__(256) calib_valu_kernel(int iters, float *sink) {
+  const int lane = threadIdx.x & 63;
+  const float m = 1.0f + 1e-7f * lane, c = 1e-9f * (lane + 1);
+  float x[VA_CHAINS];
+#pragma unroll
+  for (int j = 0; j < VA_CHAINS; j++) x[j] = 0.5f + 0.01f * j;
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int j = 0; j < VA_CHAINS; j++) x[j] = __builtin_fmaf(x[j], m, c);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < VA_CHAINS; j++) s += x[j];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // keeps the chains alive
+}
+
+// Matrix core and vector ALU together: per round, 8 independent 16x16x64 int8 MFMA chains
+// and V x 8 fp32 fused multiply-adds on 8 independent chains (no data flows between the
+// two). With V = 0 it is the MFMA rate, and the time with V > 0 against the MFMA-only and
+// VALU-only times tells how far the two units overlap.
+template <int V>
+__global__ void __launch_bounds__(256) calib_mix_kernel(int iters, float *sink) {
+  const int lane = threadIdx.x & 63;
+  const u32x4_t a = {(uint32_t)lane, 1u, 2u, 3u}, b = {3u, (uint32_t)lane, 1u, 0x01010101u};
+  const float m = 1.0f + 1e-7f * lane, c = 1e-9f * (lane + 1);
+  i32x4_t acc[MF_CHAINS] = {};
+  float x[VA_CHAINS];
+#pragma unroll
+  for (int j = 0; j < VA_CHAINS; j++) x[j] = 0.5f + 0.01f * j;
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int ch = 0; ch < MF_CHAINS; ch++) {
+      acc[ch] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                      __builtin_bit_cast(i32x4_t, b), acc[ch], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < V; v++) x[(ch * V + v) % VA_CHAINS] = __builtin_fmaf(x[(ch * V + v) % VA_CHAINS], m, c);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < MF_CHAINS; ch++) s += (float)acc[ch][0];
+#pragma unroll
+  for (int j = 0; j < VA_CHAINS; j++) s += x[j];
+  if (s == 1234.5f) sink[blockIdx.x] = s;
+}
+
+constexpr int LDS_THREADS = 1024;
+constexpr int LDS_BYTES = 128 * 1024;  // the size of one PQ table slice: [16][256][8] fp32
+
+// LDS read rate: every lane issues 16-byte reads. Pattern 0: a wave reads 1 KiB of
+// contiguous LDS (conflict-free). Pattern 1: the PQ lookup pattern: lane pairs share a
+// token, each lane reads the 16 bytes of its half of table row (m, code) of a [16][256][8]
+// fp32 table; each token has 16 random codes (a hash of its index), and every round XORs
+// them with a round-dependent byte (a bijection on codes, so they stay uniform and their
+// collisions change from round to round).
+template <int PATTERN>
+__global__ void __launch_bounds__(LDS_THREADS) calib_lds_kernel(int iters, uint32_t *sink) {
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  for (int i = threadIdx.x; i < LDS_BYTES / 16; i += LDS_THREADS)
+    reinterpret_cast<u32x4_t *>(lds)[i] = u32x4_t{(uint32_t)i, (uint32_t)i * 3u, 7u, 1u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t code[16];
+  uint32_t h = (uint32_t)(threadIdx.x >> 1) * 0x9E3779B9u + blockIdx.x * 0x85EBCA6Bu + 1u;
+#pragma unroll
+  for (int m = 0; m < 16; m++) {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    code[m] = h >> 24;
+  }
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; it++) {
+    const uint32_t r = ((uint32_t)it * 0x9E3779B9u) >> 24;  // the same in every lane
+#pragma unroll
+    for (int m = 0; m < 16; m++) {
+      uint32_t off;
+      if constexpr (PATTERN == 0)
+        off = ((uint32_t)(w * 16 + m) * 1024u + (uint32_t)it * 16384u + lane * 16u) % LDS_BYTES;
+      else
+        off = ((uint32_t)m * 256u + (code[m] ^ r)) * 32u + (lane & 1) * 16u;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(lds + off);
+      acc ^= v[0] + v[3];
+    }
+  }
+  if (acc == 0x12345678u) sink[blockIdx.x] = acc;
+}
+
+}  // namespace
+
+// Launches waves_per_simd x 4 x CUs waves of `iters` x 8 fused multiply-adds per lane;
+// *ops receives the FLOP count (2 per lane per FMA).
+extern "C" int maxsim_calib_valu(int iters, int waves_per_simd, float *sink, double *ops,
+                                 void *stream) {
+  if (!sink || !ops) return MAXSIM_ERR_NULL;
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 8) return MAXSIM_ERR_SHAPE;
+  maxsim::DeviceInfo di;
+  int rc = maxsim::current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  const int grid = di.cus * waves_per_simd;
+  *ops = 2.0 * 64 * VA_CHAINS * (double)iters * grid * 4.0;
+  hipLaunchKernelGGL(calib_valu_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+// valu_per_mfma in {0, 1, 2, 4, 8}; *ops receives the launch's int8 MFMA integer ops.
+extern "C" int maxsim_calib_mix(int valu_per_mfma, int iters, int waves_per_simd, float *sink,
+                                double *ops, void *stream) {
+  if (!sink || !ops) return MAXSIM_ERR_NULL;
+  const int V = valu_per_mfma;
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 8 ||
+      (V != 0 && V != 1 && V != 2 && V != 4 && V != 8))
+    return MAXSIM_ERR_SHAPE;
+  maxsim::DeviceInfo di;
+  int rc = maxsim::current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  const int grid = di.cus * waves_per_simd;
+  *ops = 16.0 * 16 * 64 * 2 * MF_CHAINS * (double)iters * grid * 4.0;
+  hipStream_t st = (hipStream_t)stream;
+  switch (V) {
+  case 0: hipLaunchKernelGGL(calib_mix_kernel<0>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  case 1: hipLaunchKernelGGL(calib_mix_kernel<1>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  case 2: hipLaunchKernelGGL(calib_mix_kernel<2>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  case 4: hipLaunchKernelGGL(calib_mix_kernel<4>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  default: hipLaunchKernelGGL(calib_mix_kernel<8>, dim3(grid), dim3(256), 0, st, iters, sink); break;
+  }
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}
+
+// One 1024-thread workgroup per CU with 128 KiB of LDS; *bytes receives the LDS bytes read.
+extern "C" int maxsim_calib_lds(int pattern, int iters, uint32_t *sink, double *bytes,
+                                void *stream) {
+  if (!sink || !bytes) return MAXSIM_ERR_NULL;
+  if ((pattern != 0 && pattern != 1) || iters < 1) return MAXSIM_ERR_SHAPE;
+  maxsim::DeviceInfo di;
+  int rc = maxsim::current_device(di);
+  if (rc != MAXSIM_OK) return rc;
+  if (di.max_lds < (size_t)LDS_BYTES) return MAXSIM_ERR_UNSUPPORTED;
+  auto kern = pattern == 0 ? calib_lds_kernel<0> : calib_lds_kernel<1>;
+  *bytes = 16.0 * 16 * (double)iters * LDS_THREADS * di.cus;
+  hipLaunchKernelGGL(kern, dim3(di.cus), dim3(LDS_THREADS), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
+}

@@ -6,6 +6,13 @@
 //   - s = fl32( fl32(dot_ij) * fl32(q_scale[i] * d_scale[j]) ) for int8 storage,
 //     dot_ij the exact int32 dot product (Flash-MaxSim abstract: INT8xINT8
 //     scoring; the per-token scales are applied as a product before the max).
+//     The scale products fl32(q_scale[i] * d_scale[j]) of a 16-token tile are an
+//     outer product with one term per entry: the matrix core computes them
+//     (v_mfma_f32_16x16x1_4b_f32, four 16x16 blocks with K = 1, each entry one
+//     product plus zero, rounded once to nearest even, so bit-identical to a
+//     rounded multiply) in the layout of the int32 accumulators, and the vector
+//     unit keeps one convert, one rounded multiply and half a three-way max per
+//     similarity.
 //
 // Flash-MaxSim's forward pass (Figure 1, Algorithm 2) loops over query tiles
 // inside one program per (query, document) pair; on gfx950 the query tiles run
@@ -47,6 +54,19 @@ template <> struct Elem<DT_I8> { static constexpr int bytes = 1; };
 __device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
                                                __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+}
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Four 16x16 blocks, K = 1: block k of the result, lane l, element 4k + r, is
+// a * b of lane (16k + 4 * (l / 16) + r) of the A operand and lane (16k + l % 16) of the B
+// operand: with A = the tile's 16 document-token scales (lane l: row l % 16, the same in
+// every block) and B = the scales of four query blocks (lane l: block l / 16, column
+// l % 16), element 4k + r of lane l is the scale product of accumulator element r of
+// query block k in that lane. One product plus zero per entry, rounded once.
+__device__ __forceinline__ f32x16_t scale_products(float a, float b) {
+  const f32x16_t zero = {};
+  return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, zero, 0, 0, 0);
 }
 
 template <bool INT> struct AccType { using type = f32x4_t; };
@@ -115,7 +135,16 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   // Token t of the workgroup's numbering is token t % q_pad of query t / q_pad; padding
   // tokens are zero vectors and are left out of the sums.
   u32x4_t qreg[QBW][KSB];
-  float qs[QBW];
+  // INT8 scale products on the matrix core (SP) where the registers allow: the products of
+  // a tile take 16 VGPRs per four query blocks. The widest slices (QBW * KSB > 16, d = 256
+  // and 512 with long queries) form them on the vector unit instead (no spills).
+  constexpr bool SP = I8 && QBW * KSB <= 16;
+  // SP: lane l's B operand of the scale products of query blocks 4s .. 4s + 3: the scale of
+  // column l % 16 of block 4s + l / 16 (0 for padding). Otherwise qs: the scale of the
+  // lane's column of each block.
+  constexpr int NS = SP ? (QBW + 3) / 4 : 1;
+  float qsb[NS];
+  float qs[SP ? 1 : QBW];
   // Row of Q [n_q * q_len] held by the lane's column of query block qb, or -1 (padding).
   // A 16-token block lies within one padded query, so the query index is wave-uniform.
   // (A single query: the row is the token index itself.)
@@ -128,13 +157,19 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     const int qq = tb / q_pad, pos = tb - qq * q_pad + r16;
     return qq < a.n_q && pos < q_len ? qq * q_len + pos : -1;
   };
+  static_assert(!I8 || !BATCH, "INT8 scores one query per call");
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    qsb[s] = 0.f;
+    if constexpr (SP) {
+      const int qi = q_base + (4 * s + g) * 16 + r16;
+      if (4 * s + g < QBW && qi < q_len) qsb[s] = a.q_scale[qi];
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < QBW; qb++) {
     const int row = q_row(qb);
-    qs[qb] = 0.f;
-    if constexpr (I8) {
-      if (row >= 0) qs[qb] = a.q_scale[row];
-    }
+    if constexpr (I8 && !SP) qs[qb] = row >= 0 ? a.q_scale[row] : 0.f;
 #pragma unroll
     for (int c = 0; c < KSB; c++) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -327,16 +362,27 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
       // max; with the argmax, ties keep the lowest row (the lane holds rows 4g .. 4g + 3 of
       // the tile in increasing order, and rows past the end duplicate the last token, so
       // only a strictly larger value replaces the maximum and their index is never taken)
+      // INT8: the scale products of tile t (see scale_products), from the matrix core
+      f32x16_t sp[NS];
+      auto scale_tile = [&](int t) {
+        if constexpr (SP) {
+          const float ds = dscale_lds[buf][t * 16 + r16];
+#pragma unroll
+          for (int s = 0; s < NS; s++) sp[s] = scale_products(ds, qsb[s]);
+        }
+      };
       auto fold = [&](int t, const AccT(&acc)[QBW]) {
         const int row0 = t * 16 + 4 * g;
         f32x4_t ds;
-        if constexpr (I8) ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
+        if constexpr (I8 && !SP) ds = *reinterpret_cast<const f32x4_t *>(&dscale_lds[buf][row0]);
 #pragma unroll
         for (int qb = 0; qb < QBW; qb++) {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; r++) {
-            if constexpr (I8)
+            if constexpr (SP)
+              v[r] = __fmul_rn((float)acc[qb][r], sp[qb / 4][4 * (qb % 4) + r]);
+            else if constexpr (I8)
               v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[qb], ds[r]));
             else
               v[r] = acc[qb][r];
@@ -375,7 +421,9 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
           // vector instructions per query block: INT8 ~14 (per row a convert, two products,
           // and half a three-way max), the argmax ~12 (a compare and two selects per row),
           // a plain max ~4
-          constexpr int VQB = I8 ? 14 : (ARG ? 12 : 4);
+          // INT8 ~10 per query block with the scale products on the matrix core (per row a
+          // convert and a product, and half a three-way max), 14 without
+          constexpr int VQB = SP ? 10 : I8 ? 14 : (ARG ? 12 : 4);
           constexpr int VPM = (VQB + KSB - 1) / KSB;
           __builtin_amdgcn_sched_group_barrier(0x100, KSB, 0);  // the A reads first
 #pragma unroll
@@ -389,20 +437,25 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         read_next(1);
         int t = 0;
         for (; t + 2 < ntiles; t += 2) {  // fold tiles t, t + 1; multiply t + 1, t + 2
+          scale_tile(t);
           mfma_tile(accB, an);
           read_next(t + 2);
           fold(t, accA);
           interleave();
+          scale_tile(t + 1);
           mfma_tile(accA, an);
           read_next(t + 3);
           fold(t + 1, accB);
           interleave();
         }
         if (t + 1 < ntiles) {  // two tiles left: t in accA, t + 1 in an
+          scale_tile(t);
           mfma_tile(accB, an);
           fold(t, accA);
+          scale_tile(t + 1);
           fold(t + 1, accB);
         } else {
+          scale_tile(t);
           fold(t, accA);
         }
       } else if constexpr (HALF) {
@@ -471,6 +524,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
 #pragma unroll
           for (int c = 0; c < KSB; c++) aop[c] = read_a(t, c);
           AccT acc[QBW];
+          scale_tile(t);
           mfma_tile(acc, aop);
           fold(t, acc);
         }

@@ -65,8 +65,21 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def host_threads() -> int:
+    """Host cores this process may run on (its CPU affinity), or OMP_NUM_THREADS where the
+    environment sets a smaller share."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
 def _threads(n):
-    return n if n else max(1, min(16, os.cpu_count() or 1))
+    return n if n else host_threads()
 
 
 def _c(a, dt=None):

@@ -30,6 +30,8 @@ int gen_plant_doc(uint64_t seed, uint64_t q_stream, int64_t q_row0, int nq, uint
 int gen_codebook(uint64_t seed, uint64_t stream, int M, int K, int dsub, float *C);
 int gen_codes(uint64_t seed, uint64_t stream, int64_t row0, int64_t n_tokens, int M, int K,
               uint8_t *codes);
+int gen_encoded_codes(uint64_t seed, uint64_t stream, int64_t row0, int64_t n, int M, int K,
+                      int dsub, const float *C, uint8_t *codes, int nthreads);
 int gen_pq_encode(const double *x, int64_t n, int M, int K, int dsub, const float *C,
                   uint8_t *codes);
 void gen_round_f32_to_bf16(const float *x, int64_t n, uint16_t *out);
@@ -173,6 +175,9 @@ int main(void) {
     double *x = malloc(sizeof(double) * 3 * dp);
     for (int i = 0; i < 3 * dp; i++) x[i] = sin(0.37 * i);
     check(gen_pq_encode(x, 3, M, K, dsub, C, codes), "gen_pq_encode");
+    check(gen_encoded_codes(5, 1, 0, n_docs * nd, M, K, dsub, C, codes, nthreads),
+          "gen_encoded_codes");
+    check(gen_encoded_codes(5, 1, 7, 0, M, K, dsub, C, codes, nthreads), "gen_encoded_codes n=0");
     double *T = malloc(sizeof(double) * q_len * M * K);
     check(oracle_pq_tables(Q, q_len, BF16, C, M, K, dsub, T), "oracle pq tables");
     double *out = malloc(sizeof(double) * n_docs);

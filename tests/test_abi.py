@@ -51,7 +51,8 @@ def test_every_declared_symbol_is_exported(L):
 def test_calibration_symbols_are_exported(L):
     names = declared_functions(CALIB_HEADER)
     assert {"maxsim_calib_read", "maxsim_calib_copy", "maxsim_calib_mfma",
-            "maxsim_calib_write"} <= set(names)
+            "maxsim_calib_write", "maxsim_calib_valu", "maxsim_calib_mix",
+            "maxsim_calib_lds"} <= set(names)
     out = os.popen(f"nm -D --defined-only {ms.LIB_PATH}").read()
     assert set(names) <= set(re.findall(r" T (maxsim_\w+)", out))
 
@@ -65,6 +66,16 @@ def test_calibration_argument_checks(L):
     assert f(4, 10, 1, P, ctypes.addressof(ops), None) == SHAPE
     assert f(0, 0, 1, P, ctypes.addressof(ops), None) == SHAPE
     assert f(0, 10, 9, P, ctypes.addressof(ops), None) == SHAPE
+    v, mx, lds = L.maxsim_calib_valu, L.maxsim_calib_mix, L.maxsim_calib_lds
+    v.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    mx.argtypes = [ctypes.c_int] + v.argtypes
+    lds.argtypes = v.argtypes
+    assert v(10, 1, None, ctypes.addressof(ops), None) == NULL
+    assert v(0, 1, P, ctypes.addressof(ops), None) == SHAPE
+    assert mx(3, 10, 2, P, ctypes.addressof(ops), None) == SHAPE  # 0, 1, 2, 4 or 8 per MFMA
+    assert mx(4, 10, 9, P, ctypes.addressof(ops), None) == SHAPE
+    assert lds(2, 10, P, ctypes.addressof(ops), None) == SHAPE    # pattern 0 or 1
+    assert lds(0, 10, P, None, None) == NULL
 
 
 def test_no_torch_in_signatures():

@@ -115,3 +115,17 @@ def test_codes_and_codebook():
     enc = gen.pq_encode(x, C)
     dist = ((x.reshape(50, 16, 1, 8) - C[None].astype(np.float64)) ** 2).sum(-1)
     assert np.array_equal(enc, dist.argmin(-1).astype(np.uint8))
+
+
+def test_encoded_codes_equal_nearest_centroid_of_generated_tokens():
+    """gen.encoded_codes (tokens generated and encoded in one threaded pass, centroid loop
+    innermost) gives the codes pq_encode gives for the same generated tokens, for any
+    thread count and row offset."""
+    C = gen.codebook(5)
+    x = gen.tokens(5, gen.S_DOCS, 100, 700, 128, "f64")
+    want = gen.pq_encode(x, C)
+    for nt in (1, 3, 8):
+        assert np.array_equal(gen.encoded_codes(5, gen.S_DOCS, 100, 700, C, nthreads=nt), want)
+    # with the ties-to-lowest rule, a token equal to a centroid's sub-vectors takes it
+    assert np.array_equal(gen.pq_encode(np.repeat(C[:, 3, :].reshape(1, -1).astype(np.float64), 2, 0),
+                                        C), np.full((2, 16), 3, np.uint8))
