@@ -15,14 +15,16 @@
 // k <= 128: sorted runs held by waves (bitonic top-k).
 //  * A run is 128 keys in ascending order held by one wave, two per lane (positions 2l and
 //    2l + 1 in lane l). A wave sorts its run with a bitonic network whose exchanges between
-//    lanes are register moves (DPP row and quad permutes, ds_swizzle, v_permlane32_swap):
-//    no LDS traffic and no barriers.
+//    lanes are vector-unit moves (DPP row and quad permutes, v_permlane16/32_swap): no LDS
+//    traffic and no barriers.
 //  * Two runs merge into the best 128 of their union: the elementwise minimum of one run and
 //    the other reversed is bitonic and holds those 128 keys; seven half-cleaner steps sort it.
 //  * Pass 1: a workgroup of 16 waves takes 2048 scores, each wave sorts 128 of them, and the
 //    16 runs merge in a tree through LDS (four barriers) into the chunk's best 128.
-//  * Later passes: a workgroup merges up to 64 runs (four per wave in turn, then the tree).
-//    The top-100 of 100K scores is one pass of 49 workgroups and one merge of 49 runs.
+//  * Later passes: a workgroup merges up to 64 runs (four per wave, loaded at once, then the
+//    tree). The top-100 of 100K scores is one pass of 49 workgroups and one merge of 49 runs.
+//    Two launches: each launch boundary costs about 7 us here, and merging across
+//    workgroups within one launch (device-scope fences on every workgroup) measured slower.
 // 128 < k <= 1024: a workgroup sorts 2048 keys in LDS (bitonic) and keeps k, level by level
 // until one chunk remains.
 // No atomics anywhere. Rows (queries of a batch) are independent: blockIdx.y is the row.
@@ -125,9 +127,11 @@ constexpr int RUN_CHUNK = RUN_WAVES * RUN;    // scores per workgroup of the fir
 constexpr int RUN_FANIN = 4 * RUN_WAVES;      // runs merged per workgroup of later passes
 constexpr int RUN_MAX_K = RUN;
 
-// The value of lane (lane ^ M), M < 64, as register moves: quad and row permutes (DPP) for
-// lane ^ 1, ^ 2, ^ 3, ^ 7, ^ 15, ds_swizzle (xor within 32 lanes) for the others below 32,
-// v_permlane32_swap for lane ^ 32, and the composition of the two above 32.
+// The value of lane (lane ^ M), M < 64, by vector-unit moves only (no LDS round trip):
+// quad permutes for lane ^ 1, ^ 2, ^ 3, row_half_mirror (^ 7), row_ror:8 (^ 8 within a row
+// of 16), row_mirror (^ 15), v_permlane16_swap (^ 16), v_permlane32_swap (^ 32), and their
+// compositions: ^ 4 = (^ 7)(^ 3), ^ 31 = (^ 15)(^ 16), ^ 63 = (^ 31)(^ 32). Other masks take
+// ds_swizzle (xor within 32 lanes).
 template <int M> __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   static_assert(M > 0 && M < 64, "a lane of the wave");
   if constexpr (M == 1) {
@@ -136,20 +140,27 @@ template <int M> __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
     return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
   } else if constexpr (M == 3) {
     return __builtin_amdgcn_update_dpp(0u, x, 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
+  } else if constexpr (M == 4) {
+    return lane_xor<3>(lane_xor<7>(x));
   } else if constexpr (M == 7) {
     return __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, true);  // row_ror:8
   } else if constexpr (M == 15) {
     return __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, true);  // row_mirror
-  } else if constexpr (M < 32) {
+  } else if constexpr (M == 16 || M == 32) {
+    // with x in both operands, the first result holds in the upper member of each pair of
+    // 16- (32-) lane groups the lower member's value, the second result the reverse
+    const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & M) ? p[0] : p[1];
+  } else if constexpr (M == 31) {
+    return lane_xor<15>(lane_xor<16>(x));
+  } else if constexpr (M > 32) {
+    return lane_xor<M ^ 32>(lane_xor<32>(x));
+  } else {
     // bitmask mode: lane' = ((lane & 0x1f) | 0) ^ M within each half of the wave
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (M << 10) | 0x1F);
-  } else if constexpr (M == 32) {
-    // with x in both operands, lanes 0..31 of the second result hold lanes 32..63 and
-    // lanes 32..63 of the first result hold lanes 0..31
-    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (threadIdx.x & 32) ? p[0] : p[1];
-  } else {
-    return lane_xor<M ^ 32>(lane_xor<32>(x));
   }
 }
 
@@ -168,18 +179,26 @@ struct Run {
 
 // positions 2l and 2l + 1 (within the lane)
 __device__ __forceinline__ void run_cas1(Run &r) {
-  const uint64_t lo = kmin(r.k0, r.k1), hi = kmax(r.k0, r.k1);
+  const bool sw = r.k1 < r.k0;
+  const uint64_t lo = sw ? r.k1 : r.k0, hi = sw ? r.k0 : r.k1;
   r.k0 = lo;
   r.k1 = hi;
+}
+
+// One side of a compare-exchange: the lower position keeps the smaller key, the upper one
+// the larger, so the partner's key y replaces k exactly when (y < k) == lower. (Equal keys
+// are padding, where either is the same.) One 64-bit compare and two selects per key; the
+// comparison with `lower` is an operation on lane masks.
+__device__ __forceinline__ uint64_t keep(uint64_t k, uint64_t y, bool lower) {
+  return (y < k) == lower ? y : k;
 }
 
 // Half-cleaner step of stride 2M: position p against p ^ 2M (lane ^ M, the same slot); the
 // lower position keeps the smaller key.
 template <int M> __device__ __forceinline__ void run_xor(Run &r, int lane) {
   const bool lower = (lane & M) == 0;
-  const uint64_t y0 = lane_xor64<M>(r.k0), y1 = lane_xor64<M>(r.k1);
-  r.k0 = lower ? kmin(r.k0, y0) : kmax(r.k0, y0);
-  r.k1 = lower ? kmin(r.k1, y1) : kmax(r.k1, y1);
+  r.k0 = keep(r.k0, lane_xor64<M>(r.k0), lower);
+  r.k1 = keep(r.k1, lane_xor64<M>(r.k1), lower);
 }
 
 // First step of a merge of size 2M + 2: position p against p ^ (2M + 1), its mirror within
@@ -187,8 +206,8 @@ template <int M> __device__ __forceinline__ void run_xor(Run &r, int lane) {
 template <int M> __device__ __forceinline__ void run_mirror(Run &r, int lane) {
   const bool lower = (lane & ((M + 1) >> 1)) == 0;
   const uint64_t y0 = lane_xor64<M>(r.k1), y1 = lane_xor64<M>(r.k0);
-  r.k0 = lower ? kmin(r.k0, y0) : kmax(r.k0, y0);
-  r.k1 = lower ? kmin(r.k1, y1) : kmax(r.k1, y1);
+  r.k0 = keep(r.k0, y0, lower);
+  r.k1 = keep(r.k1, y1, lower);
 }
 
 // Sort a bitonic run ascending: half-cleaners of strides 64, 32, ..., 1.
@@ -299,15 +318,29 @@ __global__ void __launch_bounds__(RUN_THREADS) topk_merge_kernel(TopkRunArgs a) 
   const int64_t row = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * RUN_FANIN + w;
   const uint64_t *runs = a.in_runs + row * a.n_runs * RUN;
-  Run r{~0ull, ~0ull};
-  if (r0 < a.n_runs) {
-    r.k0 = runs[r0 * RUN + 2 * lane];
-    r.k1 = runs[r0 * RUN + 2 * lane + 1];
-  }
+  // all of the wave's runs are loaded before the first merge (one memory latency, not four);
+  // lane l holds run j's keys at positions 2l, 2l + 1 (the first) and, reversed, at
+  // 127 - 2l, 126 - 2l (the others)
+  constexpr int PER = RUN_FANIN / RUN_WAVES;
+  uint64_t b0[PER], b1[PER];
 #pragma unroll
-  for (int j = 1; j < RUN_FANIN / RUN_WAVES; j++) {
+  for (int j = 0; j < PER; j++) {
     const int64_t rj = r0 + j * RUN_WAVES;
-    if (rj < a.n_runs) run_merge_from(r, runs + rj * RUN, lane);
+    b0[j] = b1[j] = ~0ull;
+    if (rj < a.n_runs) {
+      const uint64_t *src = runs + rj * RUN;
+      b0[j] = j == 0 ? src[2 * lane] : src[127 - 2 * lane];
+      b1[j] = j == 0 ? src[2 * lane + 1] : src[126 - 2 * lane];
+    }
+  }
+  Run r{b0[0], b1[0]};
+#pragma unroll
+  for (int j = 1; j < PER; j++) {
+    if (r0 + j * RUN_WAVES < a.n_runs) {
+      r.k0 = kmin(r.k0, b0[j]);
+      r.k1 = kmin(r.k1, b1[j]);
+      run_clean(r, lane);
+    }
   }
   run_tree_and_emit(r, a, row, lds);
 }
