@@ -112,10 +112,11 @@ def test_pq_every_document(name):
     T = oracle.pq_tables(Q, w["dtype"], C)
     if w["layout"] == "csr":
         off = gen.csr_offsets(gen.lengths(w["seed"], w["B"]))
-        codes = gen.codes(w["seed"], int(off[-1]), bench.PQ_M, bench.PQ_K)
+        # the bench's codes: nearest-centroid codes of the generated tokens
+        codes = bench.pq_codes(w["seed"], int(off[-1]), C)
         want = oracle.maxsim_pq(T, codes, offsets=off)
     else:
-        codes = gen.codes(w["seed"], w["B"] * w["nd"], bench.PQ_M, bench.PQ_K)
+        codes = bench.pq_codes(w["seed"], w["B"] * w["nd"], C)
         want = oracle.maxsim_pq(T, codes, nd=w["nd"])
     compare(got, want, tol=PQ_TOL, what=f"{name} (all docs)")
 

@@ -135,3 +135,45 @@ def test_planted_docs_rank_first_after_encoding():
     compare(got, want, tol=PQ_TOL, what="PQ planted")
     top = np.lexsort((np.arange(len(got)), -got))[:5]
     assert set(top.tolist()) == set(c.planted.tolist())
+
+
+@pytest.mark.parametrize("q_len", [5, 20, 32, 64])
+@pytest.mark.parametrize("layout", ["csr", "fixed"])
+def test_score_several_token_capped_chunks(layout, q_len):
+    """Workgroup ranges of about 12.5K tokens: with a chunk cap of 6144 tokens (the
+    MAXSIM_PQ_CHUNK_TOK knob, read at every call) three chunks each, so the slices are walked
+    up, down and up again (the slice at each chunk boundary is not staged again) with 1, 3, 4
+    or 8 slices of 8 query tokens; empty CSR documents among them. Without the cap (the
+    default) the same corpora take one chunk per workgroup, also checked, and both give the
+    same scores bit for bit (each document's arithmetic does not depend on the chunking)."""
+    import os
+    rng = np.random.default_rng(60 + q_len)
+    if layout == "csr":
+        lens = rng.integers(0, 161, size=40000).astype(np.int64)
+        lens[::97] = 0
+        off = gen.csr_offsets(lens)
+        n_tok, nd = int(off[-1]), 0
+    else:
+        off, nd = None, 80
+        n_tok = 40000 * nd
+    say(f"case: PQ {layout} q_len={q_len}, {n_tok} tokens, several chunks per workgroup")
+    C = gen.codebook(60)
+    Q = gen.tokens(60, gen.S_QUERY, 0, q_len, 128, "bf16")
+    codes = gen.codes(60 + q_len, n_tok)
+    T = gpu_tables(Q, "bf16", C)
+    Th = oracle.pq_tables(Q, "bf16", C)
+    want = oracle.maxsim_pq(Th, codes, offsets=off) if off is not None else \
+        oracle.maxsim_pq(Th, codes, nd=nd)
+    saved = os.environ.get("MAXSIM_PQ_CHUNK_TOK")
+    try:
+        os.environ["MAXSIM_PQ_CHUNK_TOK"] = "6144"
+        got = gpu_pq(T, codes, offsets=off, nd=nd)
+        os.environ["MAXSIM_PQ_CHUNK_TOK"] = "0"
+        whole = gpu_pq(T, codes, offsets=off, nd=nd)
+    finally:
+        if saved is None:
+            os.environ.pop("MAXSIM_PQ_CHUNK_TOK", None)
+        else:
+            os.environ["MAXSIM_PQ_CHUNK_TOK"] = saved
+    compare(got, want, tol=PQ_TOL, what=f"PQ {layout} q_len={q_len} several chunks")
+    assert np.array_equal(got, whole)
