@@ -480,6 +480,55 @@ def lds_ceilings(ms, achieved, median_ms):
     return out
 
 
+def calib_suite():
+    """The device's measured ceilings, one JSON line: stream read and write, sustained MFMA
+    rates, the vector-ALU rate, the matrix core and vector ALU side by side, and LDS reads."""
+    import torch
+
+    import maxsim_scoring_fwd_amd as ms
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(65536, dtype=torch.float32, device=dev)
+    usink = torch.zeros(65536, dtype=torch.int32, device=dev)
+
+    def med(fn, reps=7):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            r = fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append((a.elapsed_time(b), r))
+        ts.sort(key=lambda x: x[0])
+        return ts[len(ts) // 2]
+
+    out = {"device": torch.cuda.get_device_name(0)}
+    buf = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    t, _ = med(lambda: ms.calib_read(buf, usink))
+    out["stream_read_GBps"] = round(buf.numel() * 4 / (t * 1e-3) / 1e9, 1)
+    t, _ = med(lambda: ms.calib_write(buf))
+    out["stream_write_GBps"] = round(buf.numel() * 4 / (t * 1e-3) / 1e9, 1)
+    del buf
+    for kind, name in ((0, "bf16_16x16x32"), (1, "bf16_32x32x16"), (2, "i8_16x16x64"), (3, "i8_32x32x32")):
+        for w in (2, 4):
+            t, ops = med(lambda: ms.calib_mfma(kind, 4000, w, sink))
+            out[f"mfma_{name}_w{w}_TOPs"] = round(ops / (t * 1e-3) / 1e12, 1)
+    for w in (1, 2, 4, 8):
+        t, ops = med(lambda: ms.calib_valu(20000, w, sink))
+        out[f"valu_fp32_fma_w{w}_TFLOPs"] = round(ops / (t * 1e-3) / 1e12, 1)
+    for w in (2, 4):
+        for v in (0, 1, 2, 4, 8):
+            t, ops = med(lambda: ms.calib_mix(v, 4000, w, sink))
+            out[f"mix_w{w}_v{v}_ms"] = round(t, 4)
+    for pat, name in ((0, "contiguous"), (1, "pq_pattern")):
+        t, b = med(lambda: ms.calib_lds(pat, 2000, usink))
+        out[f"lds_read_{name}_GBps"] = round(b / (t * 1e-3) / 1e9, 1)
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(mib: int, steps: int):
     """Run the plain 128-bit copy kernel on a buffer of known size (counter calibration)."""
     import torch
@@ -506,6 +555,8 @@ def main():
     ap.add_argument("--no-calib", action="store_true", help="skip the stream-read calibration")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run the copy kernel on this many MiB, --steps times")
+    ap.add_argument("--calib-suite", action="store_true",
+                    help="only measure the device's ceilings (calibration kernels), one JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -516,6 +567,9 @@ def main():
         sys.exit(2)
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, args.steps)
+        return
+    if args.calib_suite:
+        calib_suite()
         return
 
     import torch
