@@ -73,7 +73,10 @@ enum maxsim_status {
  *   d           embedding dimension, a multiple of 32 in [MAXSIM_MIN_D, MAXSIM_MAX_D]
  *   out         fp32 [n_docs]
  * Up to 64 query tokens are scored by one wave per document with the whole query
- * resident; longer queries (up to 1024, Flash-MaxSim Figure 2: Lq = 1024) are split
+ * resident (in registers, or in LDS for rows wider than 512 bytes or more than 16 query
+ * registers per row, where ceil(q_len / 16) * 16 * (d * element bytes + 16) must fit in
+ * 160 KiB: fp32 with 49-64 tokens and d >= 640, or 33-48 tokens and d >= 864, return
+ * MAXSIM_ERR_UNSUPPORTED); longer queries (up to 1024, Flash-MaxSim Figure 2: Lq = 1024) are split
  * across the waves of a workgroup and need d * element bytes to be 64, 128, 256 or
  * 512 bytes and q_len <= 1024 * 64 / (d * element bytes), else MAXSIM_ERR_UNSUPPORTED.
  */
