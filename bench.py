@@ -162,7 +162,8 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if self._hip is not None and self._ev:
+        # events still alive at interpreter exit are left to the runtime's own teardown
+        if self._hip is not None and self._ev and not sys.is_finalizing():
             self._hip.hipEventDestroy(self._ev)
 
 
