@@ -178,6 +178,17 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     }
   }
 
+  // The query of each of the wave's blocks (wave-uniform) and whether the lane's column of
+  // it holds a token (bit qb), taken once: the work at every document's end then divides
+  // nothing by q_pad (runtime divisions are long scalar sequences).
+  int blk_q[QBW];
+  uint32_t real_bits = 0;
+#pragma unroll
+  for (int qb = 0; qb < QBW; qb++) {
+    blk_q[qb] = BATCH ? uniform((q_base + qb * 16) / q_pad) : 0;
+    if (q_row(qb) >= 0) real_bits |= 1u << qb;
+  }
+
   // ---- block sequence of this workgroup: (doc, block) in order ----
   // A cursor names block blk of document b (its first token and length); b >= n_docs ends
   // the sequence.
@@ -267,7 +278,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   int pend_q = -1;     //   and its query, or -1
   auto local_epilogue = [&](int64_t b, bool empty) {
     double s = 0.0;
-    int seg_q = uniform(q_base / q_pad), k = 0;
+    int seg_q = blk_q[0], k = 0;
     auto flush = [&]() {
       s = sum_row16(s);
       if (lane == k) {
@@ -280,12 +291,12 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QBW; qb++) {
       const float v = max_row_groups(m[qb]);
-      const int qq = uniform((q_base + qb * 16) / q_pad);
+      const int qq = blk_q[qb];
       if (qq != seg_q) {
         flush();
         seg_q = qq;
       }
-      if (q_row(qb) >= 0 && !empty) s += (double)v;
+      if (((real_bits >> qb) & 1u) && !empty) s += (double)v;
       m[qb] = -__builtin_inff();
     }
     flush();
@@ -544,7 +555,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
       // query changes (wave-uniform) the lanes reduce and the segment's sum goes to LDS slot
       // w * QBW + (first block of the segment). A query then adds its segments in order.
       double s = 0.0;
-      int seg_q = uniform(q_base / q_pad), seg_k = uniform(w * QBW);
+      int seg_q = blk_q[0], seg_k = uniform(w * QBW);
       auto flush = [&]() {
         s = sum_row16(s);
         if (lane == 0) part_lds[seg_k] = s;
@@ -583,13 +594,13 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
             }
           }
         } else {
-          const int qq = uniform((q_base + qb * 16) / q_pad);
+          const int qq = blk_q[qb];
           if (qq != seg_q) {
             flush();
             seg_q = qq;
             seg_k = uniform(w * QBW + qb);
           }
-          if (q_row(qb) >= 0 && !empty) s += (double)v;
+          if (((real_bits >> qb) & 1u) && !empty) s += (double)v;
         }
         m[qb] = -__builtin_inff();
         arg[qb] = -1;
