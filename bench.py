@@ -108,6 +108,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def boundary_events(n_steps: int, n_kernels: int, flush: bool):
+    """Event indices of the timed steps: step i records events[i][k] before its kernel k and,
+    where `closes[i]`, events[i][-1] after its last kernel. Without a cache flush between
+    steps, the event that starts a step also ends the one before (events[i][-1] is
+    events[i + 1][0]), so every kernel boundary costs one record. Returns (count, events,
+    closes); every index in range(count) is recorded exactly once."""
+    per = n_kernels + (1 if flush else 0)
+    count = n_steps * per + (0 if flush else 1)
+    events = [list(range(i * per, i * per + n_kernels + 1)) for i in range(n_steps)]
+    closes = [flush or i == n_steps - 1 for i in range(n_steps)]
+    return count, events, closes
+
+
 class TimingEvent:
     """A HIP event for timing only, on the HIP runtime torch has loaded, created with
     hipEventDisableSystemFence. Recording a default event (torch.cuda.Event) performs a
@@ -693,16 +706,14 @@ def main():
     log(f"warmup done ({args.warmup} steps)")
 
     nk = len(steps_fns)
-    # One event at every kernel boundary of the timed steps: where no cache flush sits between
-    # two steps, the event that starts a step also ends the one before (evs[i][-1] is
-    # evs[i + 1][0]), so each boundary costs one record.
-    per = nk + (1 if flush else 0)
-    pool = [TimingEvent() for _ in range(args.steps * per + (0 if flush else 1))]
-    evs = [pool[i * per: i * per + nk + 1] for i in range(args.steps)]
+    # one event at every kernel boundary of the timed steps (boundary_events)
+    n_ev, ev_idx, closes = boundary_events(args.steps, nk, flush)
+    pool = [TimingEvent() for _ in range(n_ev)]
+    evs = [[pool[j] for j in idx] for idx in ev_idx]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(evs[i], close=flush or i == args.steps - 1)
+        one_step(evs[i], close=closes[i])
         if flush:
             scratch.zero_()
     torch.cuda.synchronize()
