@@ -113,6 +113,17 @@ template <int XOR> __device__ __forceinline__ void row_pair(uint32_t x, uint32_t
   }
 }
 
+// s plus the s of lane ^ XOR (XOR 16 or 32), in every lane: both lanes of a pair get the
+// same sum (their two terms in either order, and double addition commutes exactly).
+template <int XOR> __device__ __forceinline__ double pair_sum_f64(double s) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, s);
+  uint32_t l0, l1, h0, h1;
+  row_pair<XOR>((uint32_t)u, l0, l1);
+  row_pair<XOR>((uint32_t)(u >> 32), h0, h1);
+  return __builtin_bit_cast(double, ((uint64_t)h0 << 32) | l0) +
+         __builtin_bit_cast(double, ((uint64_t)h1 << 32) | l1);
+}
+
 // Maximum over the four row groups, in every lane.
 __device__ __forceinline__ float max_row_groups(float v) {
   uint32_t a, b;

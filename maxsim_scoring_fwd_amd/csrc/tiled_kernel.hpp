@@ -302,6 +302,58 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     flush();
     pend_b = b;
   };
+  // With 4 or 8 query blocks per wave and queries of 1, 2 or 4 blocks, the document end
+  // treats every block at once. The row groups exchange their partial maxima so that row
+  // group g ends with the whole maximum of block g (and of block g + 4): v_permlane16_swap
+  // of blocks 2k and 2k + 1 leaves the pair's maximum of block 2k in the even row groups and
+  // of block 2k + 1 in the odd ones, and v_permlane32_swap does the same across the halves
+  // of the wave. Each 16-lane row then sums its block over the query tokens in double, and
+  // the rows of one query's blocks add their sums. One exchange and one row sum serve four
+  // blocks, where the form above reduces every block over the row groups and then every
+  // query over the lanes. The same terms are summed in another order (in double), so the two
+  // forms agree to the rounding of the fp32 scores.
+  constexpr bool EPI4 = BATCH && (QBW == 4 || QBW == 8);
+  const int bpq = q_pad / 16;  // blocks per query
+  const bool epi4 = EPI4 && local && (bpq == 1 || bpq == 2 || bpq == 4);
+  const int bpq_log = bpq == 4 ? 2 : (bpq == 2 ? 1 : 0);
+  auto local_epilogue4 = [&](int64_t b, bool empty) {
+    if constexpr (EPI4) {
+      constexpr int NP = QBW / 2, NX = QBW / 4;
+      float pm[NP];  // even row groups: block 2k, odd: block 2k + 1, over the pair
+#pragma unroll
+      for (int k = 0; k < NP; k++) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(m[2 * k]),
+                                                        __float_as_uint(m[2 * k + 1]), false, false);
+        pm[k] = __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+      }
+#pragma unroll
+      for (int k = 0; k < NX; k++) {
+        // row group g: the maximum of column r16 of block 4k + g over all four row groups
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[2 * k]),
+                                                        __float_as_uint(pm[2 * k + 1]), false, false);
+        const float x = __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        const int blk_g = 4 * k + g;
+        double s = ((real_bits >> blk_g) & 1u) ? (double)x : 0.0;
+        s = sum_row16(s);
+        if (bpq >= 2) s = pair_sum_f64<16>(s);
+        if (bpq == 4) s = pair_sum_f64<32>(s);
+        // lane k of the first row group of each query records its score
+        if (r16 == k && (g & (bpq - 1)) == 0) {
+          pend_v = empty ? -__builtin_inff() : (float)s;
+          pend_q = blk_q[0] + (blk_g >> bpq_log);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QBW; qb++) m[qb] = -__builtin_inff();
+      pend_b = b;
+    }
+  };
+  auto doc_epilogue = [&](int64_t b, bool empty) {
+    if (epi4)
+      local_epilogue4(b, empty);
+    else
+      local_epilogue(b, empty);
+  };
   auto local_store = [&]() {
     if (pend_q >= 0 && pend_q < a.n_q) a.out[(int64_t)pend_q * a.n_docs + pend_b] = pend_v;
     pend_q = -1;
@@ -338,7 +390,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
     if constexpr (BATCH) {
       if (local) {
         if (pend_epi) {
-          local_epilogue(pend_epi_b, pend_empty);
+          doc_epilogue(pend_epi_b, pend_empty);
           pend_epi = false;
         }
         local_store();
@@ -548,7 +600,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
         pend_epi_b = b;
         pend_empty = empty;
       } else {
-        local_epilogue(b, empty);
+        doc_epilogue(b, empty);
       }
     } else if (doc_end) {
       // Each lane adds its maxima over consecutive blocks of one query in double; where the
@@ -627,7 +679,7 @@ __global__ void __launch_bounds__(NW * WAVE) tiled_maxsim_kernel(TiledArgs a) {
   }
   if constexpr (BATCH) {
     if (local) {
-      if (pend_epi) local_epilogue(pend_epi_b, pend_empty);
+      if (pend_epi) doc_epilogue(pend_epi_b, pend_empty);
       local_store();
     }
   }

@@ -43,6 +43,17 @@ CASES = [  # n_q, q_len, d, dtype, layout
     (6, 33, 128, "fp32", "fixed"),    # fp32 rows of 512 B: 512 tokens per launch
     (17, 1, 128, "bf16", "csr"),      # one-token queries
     (3, 1024, 128, "bf16", "fixed"),  # one query per launch
+    # 4 or 8 query blocks per wave, queries of 1, 2 or 4 blocks: the row groups exchange
+    # their maxima so that each sums one block (the four-block document end)
+    (8, 32, 128, "bf16", "fixed"),    # 4 blocks per wave, 2 per query
+    (16, 16, 128, "bf16", "csr"),     # 4 blocks per wave, 1 per query
+    (4, 64, 128, "bf16", "csr"),      # 4 blocks per wave, 4 per query
+    (7, 32, 128, "bf16", "csr"),      # the last wave's second query is padding
+    (64, 16, 128, "bf16", "fixed"),   # 8 blocks per wave, 1 per query
+    (16, 64, 128, "fp16", "csr"),     # 8 blocks per wave, 4 per query
+    (29, 32, 128, "bf16", "csr"),     # 8 blocks per wave, padding queries in the last wave
+    (8, 30, 128, "bf16", "csr"),      # 4 blocks per wave: padding tokens in every query
+    (32, 20, 128, "bf16", "fixed"),   # 8 blocks per wave: padding tokens in every query
 ]
 
 
