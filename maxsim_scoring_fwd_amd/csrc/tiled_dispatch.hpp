@@ -11,12 +11,15 @@ inline int tiled_tokens(const TiledArgs &a) { return a.n_q * ((a.q_len + 15) & ~
 
 // Waves per workgroup. Every wave reads each A operand of a block from LDS and multiplies it
 // by its QBW query blocks, so few blocks per wave leave the kernel bound by LDS reads, and with
-// 8 waves a short query leaves some waves holding only padding. Up to 384 query tokens (dense
-// storage, within the register budget) run 4 waves of ceil(tokens / 64) blocks, two
-// workgroups per CU; longer queries and INT8 run 8 waves.
+// 8 waves a short query leaves some waves holding only padding. Up to 384 query tokens (within
+// the register budget) run 4 waves of ceil(tokens / 64) blocks, two workgroups per CU; longer
+// queries run 8 waves. INT8 rows of 64 bytes keep 8 waves (one thread per block row stages
+// the per-token scales: 512 rows). Measured for INT8 with 100K documents of 128 tokens, 8
+// against 4 waves, d = 128 / 256: 32 tokens 0.670 / 0.757 -> 0.506 / 0.556 ms, 128 tokens
+// 0.589 / 0.796 -> 0.537 / 0.716 ms, 384 tokens 0.938 / 1.451 -> 0.915 / 1.314 ms.
 inline int tiled_waves(int tokens, int ksb, bool i8) {
   const int qbw4 = (tokens + 63) / 64;
-  return !i8 && tokens <= 384 && qbw4 * ksb <= 32 ? 4 : TILED_WAVES;
+  return tokens <= 384 && qbw4 * ksb <= 32 && (!i8 || ksb >= 2) ? 4 : TILED_WAVES;
 }
 
 // Query blocks per wave for a number of query tokens (nw waves x 16 tokens x QBW >= tokens).
@@ -65,7 +68,7 @@ int tiled_by_qbw(int qbw, const TiledArgs &a, const DeviceInfo &di, hipStream_t 
 template <int DT, int KSB, bool ARG, bool BATCH>
 int tiled_by_waves(int tokens, const TiledArgs &a, const DeviceInfo &di, hipStream_t st) {
   const int nw = tiled_waves(tokens, KSB, DT == DT_I8);
-  if constexpr (DT != DT_I8) {
+  if constexpr (DT != DT_I8 || KSB >= 2) {
     if (nw == 4) return tiled_by_qbw<DT, KSB, ARG, BATCH, 4>(tiled_qbw(tokens, 4), a, di, st);
   }
   return tiled_by_qbw<DT, KSB, ARG, BATCH, TILED_WAVES>(tiled_qbw(tokens, TILED_WAVES), a, di, st);

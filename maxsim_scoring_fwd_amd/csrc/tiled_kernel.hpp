@@ -16,7 +16,7 @@
 //
 // Flash-MaxSim's forward pass (Figure 1, Algorithm 2) loops over query tiles
 // inside one program per (query, document) pair; on gfx950 the query tiles run
-// concurrently instead: the NW waves of a workgroup (8, or 4 for short queries)
+// concurrently instead: the NW waves of a workgroup (8, or 4 for queries of up to 384 tokens)
 // each hold one slice of the query tokens as resident MFMA B operands (QBW blocks
 // of 16 tokens), and one copy of every document block sits in LDS for all of them.
 //  * Documents are walked by workgroup (grid stride). A block is 32 KiB of

@@ -107,12 +107,20 @@ def check_i8(c, what):
     assert np.array_equal(gpu_i8(c, with_tok=False), got)
 
 
-@pytest.mark.parametrize("q_len", [1, 16, 32, 100, 1024])
+@pytest.mark.parametrize("q_len", [1, 16, 32, 100, 256, 384, 385, 1024])
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_int8_fixed(q_len, d):
     say(f"case: int8 q_len={q_len} d={d} B=11 Nd=150")
     c = gen.fixed_corpus(300 + q_len + d, 11, q_len, 150, d, "i8")
     check_i8(c, f"i8 q={q_len} d={d}")
+
+
+@pytest.mark.parametrize("q_len", [64, 256, 257, 512])
+def test_int8_rows_of_512_bytes(q_len):
+    """d = 512: 4 waves up to 256 query tokens, 8 beyond."""
+    say(f"case: int8 q_len={q_len} d=512 B=7 Nd=40")
+    c = gen.fixed_corpus(340 + q_len, 7, q_len, 40, 512, "i8")
+    check_i8(c, f"i8 q={q_len} d=512")
 
 
 def test_int8_colpali_shape():
