@@ -58,6 +58,7 @@ WORKLOADS = {
     "colpali-bf16-b10k": dict(_CB, B=10_000, q_len=1024, nd=1024, seed=4, pool=2_048),
     "colpali-bf16-b50k": dict(_CB, B=50_000, q_len=1024, nd=1024, seed=4, pool=2_048),
     "colpali-bf16-b175k": dict(_CB, B=175_000, q_len=1024, nd=1024, seed=4, pool=2_048),
+    "colbert-i8-b100k": dict(_CB, B=100_000, dtype="i8", path="i8"),
     "colpali-i8-b1k": dict(_CB, B=1_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8"),
     "colpali-i8-b10k": dict(_CB, B=10_000, q_len=1024, nd=1024, seed=4, dtype="i8", path="i8",
                             pool=2_048),
@@ -82,7 +83,7 @@ DEFAULT = "colbert-b100k"
 # backward's dD kernel (training step)
 KERNEL_SOURCES = {
     "dense": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "dense_variants.hpp",
-              "dense_dispatch.hpp", "dense_bf16.hip"],
+              "dense_dispatch.hpp", "dense_bf16.hip", "dense_i8.hip"],
     "train": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "backward_kernel.hpp",
               "backward.hip"],
     "tiled": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "tiled_kernel.hpp",
@@ -91,13 +92,19 @@ KERNEL_SOURCES = {
 }
 
 
+def short_query(w) -> bool:
+    """Queries of up to 64 tokens go to the one-wave-per-document dense kernel (INT8 only at
+    d = 64, 128 or 256); longer ones to the query-tiled kernel."""
+    return w["q_len"] <= 64 and (w["dtype"] != "i8" or w["d"] in (64, 128, 256))
+
+
 def kernel_family(w) -> str:
     """Which kernel sources a workload's scoring runs: the one-wave-per-document dense
-    kernel (up to 64 query tokens), the query-tiled kernel (longer queries, INT8, several
-    queries per pass), the PQ kernels, or the training step's backward."""
+    kernel (short queries), the query-tiled kernel (longer queries, several queries per
+    pass), the PQ kernels, or the training step's backward."""
     if w["path"] in ("train", "pq"):
         return w["path"]
-    if w["path"] in ("i8", "batch") or w["q_len"] > 64:
+    if w["path"] == "batch" or not short_query(w):
         return "tiled"
     return "dense"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -202,7 +209,7 @@ def bound_of(w):
         return "hbm"  # the dD kernel: writes one gradient row per document token
     if w["path"] == "pq":
         return "lds"
-    if w["path"] == "i8" or w["q_len"] > 64:
+    if not short_query(w):
         return "mfma"
     return "hbm"
 
@@ -330,6 +337,8 @@ def work_per_launch(w, inp):
         return train_dd_bytes(w, inp), "GB/s"
     if bound == "hbm":
         b = n_tok * d * esize(w["dtype"]) + q * d * esize(w["dtype"]) + B * 4
+        if w["dtype"] == "i8":
+            b += (n_tok + q) * 4  # fp32 scale per token
         if inp["offsets"] is not None:
             b += (B + 1) * 8
         return b, "GB/s"

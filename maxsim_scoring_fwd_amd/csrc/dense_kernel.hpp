@@ -1,4 +1,4 @@
-// Dense MaxSim kernel (bf16 / fp16 / fp32 storage, fixed or CSR documents).
+// Dense MaxSim kernel (bf16 / fp16 / fp32 / int8 storage, fixed or CSR documents).
 //
 // What it computes (TileMaxSim deep reading, section 1; Flash-MaxSim Figure 1):
 //   out[b] = sum_i max_j <q_i, d_j>, one fp32 score per document, with the
@@ -40,6 +40,11 @@
 //    one VGPR per 16-query block (Flash-MaxSim Figure 1: running max m, fp32
 //    accumulator). At the document's end, two cross-lane max steps and a
 //    16-lane sum give the score; one lane stores it.
+//  * INT8 storage (Flash-MaxSim abstract: INT8 x INT8 with per-token scales): the tile
+//    product is the exact int32 dot on the int8 matrix core (16x16x64, the same 64-byte
+//    chunks and operand layout), and each similarity is fl32(fl32(dot) * fl32(q_scale[i] *
+//    d_scale[j])) before the max, as in the query-tiled kernel. The scales of a lane's four
+//    rows travel with the tile's loads in the ring.
 //  * With ARG the kernel also writes each query token's maximum and the lowest
 //    document index reaching it (the argmax the Flash-MaxSim backward pass
 //    reuses): rows are folded in increasing order with a strict comparison, and
@@ -64,6 +69,8 @@ struct DenseArgs {
   float *tok_max;          // ARG only: per-token maxima [n_docs][q_len]
   int32_t *tok_arg;        // ARG only: per-token argmax [n_docs][q_len]
   int contiguous = 0;      // fixed layout: wave w takes documents [B*w/W, B*(w+1)/W)
+  const float *q_scale = nullptr;  // INT8: per query token
+  const float *d_scale = nullptr;  // INT8: per document token (the rows of D)
 };
 
 constexpr int DENSE_THREADS = 256;
@@ -159,6 +166,9 @@ struct Slot {
 template <int DT, int KSB, int QB, int P, bool QLDS, int LM, bool ARG>
 __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr bool I8 = DT == DT_I8;
+  static_assert(!I8 || !QLDS, "INT8 keeps the query in registers (one d block)");
+  using AccT = typename AccType<I8>::type;
   constexpr int PPR = KSB * 4;  // 16-byte pieces per row of one d block
   static_assert(LM != LOAD_STAGED || (PPR & (PPR - 1)) == 0, "staged tiles need 2^k pieces");
   const int lane = threadIdx.x & (WAVE - 1);
@@ -187,7 +197,14 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         qreg[qb][c] = v;
       }
     }
-  } else {
+  }
+  // INT8: the scale of the lane's query column of each block (0 for padding)
+  float qs[I8 ? QB : 1];
+  if constexpr (I8) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) qs[qb] = qb * 16 + r16 < q_len ? a.q_scale[qb * 16 + r16] : 0.f;
+  }
+  if constexpr (QLDS) {
     const int64_t per_row = RB / 16;
     const int64_t total = (int64_t)QB * 16 * per_row;
     for (int64_t idx = threadIdx.x; idx < total; idx += DENSE_THREADS) {
@@ -223,10 +240,12 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
 
   u32x4_t buf[P][KSB];
   Slot slot[P];
+  f32x4_t dsc[I8 ? P : 1];  // INT8: scales of the lane's rows 4g .. 4g + 3 of each slot's tile
 
-  auto issue = [&](u32x4_t(&dst)[KSB], Slot &sl) {
+  auto issue = [&](u32x4_t(&dst)[KSB], Slot &sl, f32x4_t &ds) {
     sl.valid = false;
     const char *base = a.Q;  // in-bounds dummy source for empty or exhausted slots
+    const float *sbase = a.q_scale;  // INT8: the tile's first row scale, or a dummy
     int last = 0;            // last valid row of the tile
     if (pb < pend) {
       sl.valid = true;
@@ -240,6 +259,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         const int64_t rem = plen - 1 - t0;
         last = rem < 15 ? (int)rem : 15;
         base = a.D + (pfirst + t0) * RB + (int64_t)pk * KSB * 64;
+        if constexpr (I8) sbase = a.d_scale + pfirst + t0;
         const int64_t ntiles = (plen + 15) >> 4;
         sl.dblk = pk;
         sl.tile = (int)ptile;
@@ -276,19 +296,26 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       for (int c = 0; c < KSB; c++)
         dst[c] = LM == LOAD_DIRECT_NT ? load16_nt(base + off + c * 64) : load16(base + off + c * 64);
     }
+    if constexpr (I8) {
+      // rows past the tile's last one take its scale, as their tokens duplicate it
+#pragma unroll
+      for (int r = 0; r < 4; r++) ds[r] = sbase[4 * g + r < last ? 4 * g + r : last];
+    } else {
+      (void)ds;
+    }
   };
 
 #pragma unroll
-  for (int p = 0; p < P; p++) issue(buf[p], slot[p]);
+  for (int p = 0; p < P; p++) issue(buf[p], slot[p], dsc[I8 ? p : 0]);
 
-  f32x4_t acc[QB];
+  AccT acc[QB];
   float m[QB];
   int arg[ARG ? QB : 1];
 #pragma unroll
   for (int qb = 0; qb < QB; qb++) {
     m[qb] = -__builtin_inff();
     if constexpr (ARG) arg[qb] = -1;
-    acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[qb] = AccT{0, 0, 0, 0};
   }
 
   for (;;) {
@@ -314,7 +341,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       }
       if (slot[p].first_blk) {
 #pragma unroll
-        for (int qb = 0; qb < QB; qb++) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; qb++) acc[qb] = AccT{0, 0, 0, 0};
       }
 #pragma unroll
       for (int c = 0; c < KSB; c++) {
@@ -326,10 +353,36 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
                 lds + (qb * 16 + r16) * QROWB + ((int64_t)slot[p].dblk * KSB + c) * 64 + g * 16);
           else
             qv = qreg[qb][c];
-          acc[qb] = ChunkMfma<DT>::run(aop[c], qv, acc[qb]);
+          if constexpr (I8)
+            acc[qb] = chunk_mfma_i8(aop[c], qv, acc[qb]);
+          else
+            acc[qb] = ChunkMfma<DT>::run(aop[c], qv, acc[qb]);
         }
       }
-      if (slot[p].last_blk) {
+      if constexpr (I8) {
+        if (slot[p].last_blk) {
+          // fl32(fl32(dot) * fl32(q_scale * d_scale)) per similarity, then as below
+          const int row0 = slot[p].tile * 16 + 4 * g;
+#pragma unroll
+          for (int qb = 0; qb < QB; qb++) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+              v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[I8 ? qb : 0], dsc[I8 ? p : 0][r]));
+            if constexpr (ARG) {
+#pragma unroll
+              for (int r = 0; r < 4; r++)
+                if (v[r] > m[qb]) {
+                  m[qb] = v[r];
+                  arg[qb] = row0 + r;
+                }
+            } else {
+              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[0]), v[1]);
+              m[qb] = __builtin_fmaxf(__builtin_fmaxf(m[qb], v[2]), v[3]);
+            }
+          }
+        }
+      } else if (slot[p].last_blk) {
         if constexpr (ARG) {
           // lane holds rows 4g .. 4g + 3 of the tile, in increasing order
           const int row0 = slot[p].tile * 16 + 4 * g;
@@ -372,7 +425,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
         if (slot[p].empty) s = -__builtin_inff();
         if (lane == 0) a.out[slot[p].doc] = s;
       }
-      issue(buf[p], slot[p]);
+      issue(buf[p], slot[p], dsc[I8 ? p : 0]);
     }
   }
 done:

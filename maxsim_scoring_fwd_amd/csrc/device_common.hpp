@@ -21,6 +21,21 @@ template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_FP16> { static constexpr int bytes = 2; };
 template <> struct Elem<DT_FP32> { static constexpr int bytes = 4; };
 
+// INT8 storage: int32 dot products on the matrix core, per-token fp32 scales applied
+// before the max (Flash-MaxSim abstract: INT8 x INT8 scoring).
+constexpr int DT_I8 = 3;
+template <> struct Elem<DT_I8> { static constexpr int bytes = 1; };
+
+// 16x16x64 i8 -> i32, K = 64 int8 = one 64-byte chunk per row (the chunk layout below).
+__device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                               __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+}
+
+// Accumulator of one 16x16 tile: fp32, or int32 for INT8.
+template <bool INT> struct AccType { using type = f32x4_t; };
+template <> struct AccType<true> { using type = i32x4_t; };
+
 // One "chunk" = 16 bytes per lane, 64 lanes: 16 rows x 64 contiguous bytes.
 // Lane l holds row (l % 16) and bytes [16*(l/16), 16*(l/16)+16) of the row's
 // 64-byte piece. chunk_mfma folds one chunk of the doc tile (operand A, rows =

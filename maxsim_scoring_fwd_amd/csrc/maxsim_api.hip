@@ -140,6 +140,15 @@ int maxsim_score_i8(const int8_t *Q, const float *q_scale, int q_len, const int8
   DeviceInfo di;
   int rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
+  if (q_len <= 64 && (d == 64 || d == 128 || d == 256)) {
+    // One wave per document with the query in registers, as for 16-bit storage: the
+    // document stream, not the matrix core, bounds these shapes.
+    DenseArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs,
+                doc_offsets ? 0 : nd, nullptr, 1, out, tok_max, tok_arg};
+    a.q_scale = q_scale;
+    a.d_scale = d_scale;
+    return dense_i8_run(d / 64, (q_len + 15) / 16, a, di, (hipStream_t)stream);
+  }
   TiledArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs, nd, nullptr, q_scale,
               d_scale, out, tok_max, tok_arg};
   return tiled_i8_run(a, d, di, (hipStream_t)stream);

@@ -44,17 +44,8 @@
 
 namespace maxsim {
 
-constexpr int DT_I8 = 3;
 constexpr int TILED_WAVES = 8;  // default waves per workgroup (query slices)
 constexpr int TILED_BLOCK_BYTES = 32 * 1024;
-
-template <> struct Elem<DT_I8> { static constexpr int bytes = 1; };
-
-// INT8: 16x16x64 i8 -> i32, K = 64 int8 = one 64-byte chunk per row.
-__device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
-                                               __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
-}
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -68,9 +59,6 @@ __device__ __forceinline__ f32x16_t scale_products(float a, float b) {
   const f32x16_t zero = {};
   return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, zero, 0, 0, 0);
 }
-
-template <bool INT> struct AccType { using type = f32x4_t; };
-template <> struct AccType<true> { using type = i32x4_t; };
 
 struct TiledArgs {
   const char *Q;

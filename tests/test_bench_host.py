@@ -65,7 +65,18 @@ def test_matrix_core_work_counts_every_query():
     assert unit == "TOP/s" and work == 2 * 1024 * 10_000 * 1024 * 128
 
 
+def test_int8_short_query_bytes_count_the_scales():
+    """INT8 ColBERT shape: one byte per element plus an fp32 scale per document and query
+    token, the fp32 score per document."""
+    w = bench.WORKLOADS["colbert-i8-b100k"]
+    work, unit = bench.work_per_launch(w, _inputs(w))
+    assert unit == "GB/s"
+    assert work == 100_000 * 128 * (128 + 4) + 32 * (128 + 4) + 100_000 * 4
+    assert bench.kernel_family(w) == "dense"
+
+
 @pytest.mark.parametrize("name,bound", [("colbert-b100k", "hbm"), ("csr-bf16", "hbm"),
+                                        ("colbert-i8-b100k", "hbm"),
                                         ("colpali-bf16-b10k", "mfma"), ("colpali-i8-b10k", "mfma"),
                                         ("batch-colbert-q8-b100k", "mfma"), ("csr-pq", "lds"),
                                         ("train-csr", "hbm")])

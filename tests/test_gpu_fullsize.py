@@ -80,7 +80,8 @@ def _sampled(name, n=600, seed=0):
 
 @pytest.mark.parametrize("name", ["colbert-b1k", "colbert-b10k", "colbert-b500k", "colbert-nd32",
                                   "colbert-nd64", "colbert-nd256", "colbert-nd512", "colbert-fp16",
-                                  "colbert-fp32", "dtile-d64", "dtile-d256", "dtile-d768"])
+                                  "colbert-fp32", "dtile-d64", "dtile-d256", "dtile-d768",
+                                  "colbert-i8-b100k"])
 def test_fixed_workloads_sampled(name):
     _sampled(name)
 
