@@ -71,6 +71,7 @@ struct DenseArgs {
   int contiguous = 0;      // fixed layout: wave w takes documents [B*w/W, B*(w+1)/W)
   const float *q_scale = nullptr;  // INT8: per query token
   const float *d_scale = nullptr;  // INT8: per document token (the rows of D)
+  int n_q = 1;                     // several-query kernel: queries [n_q][q_len] in Q
 };
 
 constexpr int DENSE_THREADS = 256;

@@ -26,6 +26,14 @@ int dense_run(DenseArgs a, int d, int dtype, hipStream_t st) {
   const int chunks = d * eb / 64;          // 64-byte pieces per token row
   const int qb = (a.q_len + 15) / 16;      // 16-query blocks
   static const int force_lds = env_knob("MAXSIM_DENSE_QLDS", 0);
+  // 5 to 16 query blocks of two-byte rows of 128 or 256 bytes (no per-token outputs): the
+  // several-query kernel with one query, the query in LDS and each wave on one document.
+  // MAXSIM_BATCH_DENSE=0 keeps them on the query-tiled kernel (for A/B measurements).
+  static const int batch_ok = env_knob("MAXSIM_BATCH_DENSE", 1);
+  if (qb > 4 && !arg && batch_ok && dense_batch_fits(1, a.q_len, d, dtype)) {
+    a.n_q = 1;
+    return dense_batch_run(a, d, dtype, di, st);
+  }
   if (qb > 4) {
     // Long queries: query slices across the waves of a workgroup.
     TiledArgs t{a.Q, a.q_len, a.D, a.offsets, a.n_docs, a.nd, a.doc_lens, nullptr, nullptr,
@@ -110,9 +118,25 @@ int maxsim_score_batch(const void *Q, int n_q, int q_len, const void *D,
   const int group = tiled_max_q(ksb) / q_pad;  // queries per pass over the documents
   if (group < 1) return MAXSIM_ERR_UNSUPPORTED;
   if (n_docs == 0) return MAXSIM_OK;
+  if (n_q == 1) {
+    // the single-query kernels, so that a batch of one equals maxsim_score bit for bit
+    DenseArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs,
+                doc_offsets ? 0 : nd, nullptr, 1, out};
+    return dense_run(a, d, dtype, (hipStream_t)stream);
+  }
   DeviceInfo di;
   rc = current_device(di);
   if (rc != MAXSIM_OK) return rc;
+  // Up to 16 blocks of query tokens (two-byte rows of 128 or 256 bytes): the
+  // one-wave-per-document kernel with the queries in LDS. MAXSIM_BATCH_DENSE=0 forces the
+  // query-tiled kernel (for A/B measurements).
+  static const int dense_ok = env_knob("MAXSIM_BATCH_DENSE", 1);
+  if (dense_ok && dense_batch_fits(n_q, q_len, d, dtype)) {
+    DenseArgs a{(const char *)Q, q_len, (const char *)D, doc_offsets, n_docs,
+                doc_offsets ? 0 : nd, nullptr, 1, out};
+    a.n_q = n_q;
+    return dense_batch_run(a, d, dtype, di, (hipStream_t)stream);
+  }
   const int64_t q_bytes = (int64_t)q_len * d * elem_bytes(dtype);
   for (int q0 = 0; q0 < n_q; q0 += group) {
     TiledArgs a{(const char *)Q + q0 * q_bytes, q_len, (const char *)D, doc_offsets, n_docs,
