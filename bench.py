@@ -86,6 +86,8 @@ KERNEL_SOURCES = {
               "dense_dispatch.hpp", "dense_bf16.hip", "dense_i8.hip"],
     "train": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "backward_kernel.hpp",
               "backward.hip"],
+    "dbatch": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "dense_dispatch.hpp",
+               "dense_batch_kernel.hpp", "dense_batch.hip"],
     "tiled": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "tiled_kernel.hpp",
               "tiled_dispatch.hpp", "tiled_dense.hip", "tiled_i8.hip", "tiled_batch.hip"],
     "pq": ["device_common.hpp", "host_common.hpp", "dense_kernel.hpp", "pq_kernel.hpp"],
@@ -98,15 +100,25 @@ def short_query(w) -> bool:
     return w["q_len"] <= 64 and (w["dtype"] != "i8" or w["d"] in (64, 128, 256))
 
 
+def dense_batch_fits(w) -> bool:
+    """Up to 16 blocks of 16 query tokens (each query padded to whole blocks) with bf16 /
+    fp16 rows of 128 or 256 bytes: the one-wave-per-document kernel with the queries in
+    LDS."""
+    row = w["d"] * esize(w["dtype"])
+    blocks = w.get("n_q", 1) * -(-w["q_len"] // 16)
+    return w["dtype"] in ("bf16", "fp16") and row in (128, 256) and blocks <= 16
+
+
 def kernel_family(w) -> str:
     """Which kernel sources a workload's scoring runs: the one-wave-per-document dense
-    kernel (short queries), the query-tiled kernel (longer queries, several queries per
-    pass), the PQ kernels, or the training step's backward."""
+    kernel (short queries), the document-stationary kernel with the queries in LDS (up to
+    16 query blocks), the query-tiled kernel (the rest), the PQ kernels, or the training
+    step's backward."""
     if w["path"] in ("train", "pq"):
         return w["path"]
-    if w["path"] == "batch" or not short_query(w):
-        return "tiled"
-    return "dense"
+    if w["path"] != "batch" and short_query(w):
+        return "dense"
+    return "dbatch" if dense_batch_fits(w) else "tiled"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PQ_M, PQ_K, PQ_DSUB = 16, 256, 8
 
@@ -202,16 +214,23 @@ def esize(dtype):
     return {"bf16": 2, "fp16": 2, "fp32": 4, "i8": 1}[dtype]
 
 
+def intensity(w) -> float:
+    """Matrix-core operations per byte of the document stream: 2 * n_q * q_len * d per token
+    of d * element bytes (plus the fp32 scale of an INT8 token)."""
+    row = w["d"] * esize(w["dtype"]) + (4 if w["dtype"] == "i8" else 0)
+    return 2.0 * w.get("n_q", 1) * w["q_len"] * w["d"] / row
+
+
 def bound_of(w):
-    if w["path"] == "batch":
-        return "mfma"  # n_q * q_len FLOP per document byte
+    """The roofline that bounds the scoring kernel: HBM below the ridge point (peak
+    operations per second over 8 TB/s), the matrix core above it; the training step's dD
+    kernel writes a gradient row per token (HBM), PQ lookups read LDS."""
     if w["path"] == "train":
-        return "hbm"  # the dD kernel: writes one gradient row per document token
+        return "hbm"
     if w["path"] == "pq":
         return "lds"
-    if not short_query(w):
-        return "mfma"
-    return "hbm"
+    ridge = MFMA_PEAK_TFLOPS[w["dtype"]] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if intensity(w) > ridge else "hbm"
 
 
 def _fill_rows(dst, seed, row0_of, nrows_total, d, dtype, device, chunk_rows, scale_dst=None):
@@ -336,7 +355,8 @@ def work_per_launch(w, inp):
     if w["path"] == "train":
         return train_dd_bytes(w, inp), "GB/s"
     if bound == "hbm":
-        b = n_tok * d * esize(w["dtype"]) + q * d * esize(w["dtype"]) + B * 4
+        n_q = w.get("n_q", 1)
+        b = n_tok * d * esize(w["dtype"]) + n_q * (q * d * esize(w["dtype"]) + B * 4)
         if w["dtype"] == "i8":
             b += (n_tok + q) * 4  # fp32 scale per token
         if inp["offsets"] is not None:
@@ -369,7 +389,7 @@ def hbm_bytes(w, inp):
         fwd = inp["n_tokens"] * d * e + B * 4 + B * q * 8
         return fwd + B * q * (d * e + 4) + train_dd_bytes(w, inp)
     b = inp["n_tokens"] * (w["d"] * esize(w["dtype"]) + (4 if w["dtype"] == "i8" else 0))
-    return b + w["B"] * 4
+    return b + w.get("n_q", 1) * w["B"] * 4
 
 
 def launches(ms, w, inp, out):
@@ -811,6 +831,11 @@ def main():
             context["frac_of_stream_read"] = round(achieved / stream_gbs, 4)
         del buf
         log(f"stream-read ceiling {stream_gbs:.0f} GB/s")
+    if bound == "hbm" and w["path"] != "train" and intensity(w) > 64:
+        # close to the ridge: the matrix-core rate beside the HBM rate
+        mfma_tops = 2 * n_q * w["q_len"] * inp["n_tokens"] * w["d"] / (avg_dom * 1e-3) / 1e12
+        context["mfma_TOPs"] = round(mfma_tops, 1)
+        context["frac_of_mfma_peak"] = round(mfma_tops / MFMA_PEAK_TFLOPS[w["dtype"]], 4)
 
     cpu = None
     if args.cpu_budget > 0:

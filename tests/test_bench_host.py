@@ -65,6 +65,18 @@ def test_matrix_core_work_counts_every_query():
     assert unit == "TOP/s" and work == 2 * 1024 * 10_000 * 1024 * 128
 
 
+def test_several_query_pass_below_the_ridge_counts_bytes():
+    """8 ColBERT queries of 32 tokens: 256 FLOP per document byte, below the bf16 ridge
+    (2.5 PFLOP/s over 8 TB/s = 312.5), so HBM bounds it; every query and score counts."""
+    w = bench.WORKLOADS["batch-colbert-q8-b100k"]
+    assert bench.intensity(w) == 256.0
+    work, unit = bench.work_per_launch(w, _inputs(w))
+    assert unit == "GB/s"
+    assert work == 100_000 * 128 * 256 + 8 * (32 * 128 * 2 + 100_000 * 4)
+    assert bench.kernel_family(w) == "dbatch"
+    assert bench.kernel_family(bench.WORKLOADS["batch-colbert-q32-b100k"]) == "tiled"
+
+
 def test_int8_short_query_bytes_count_the_scales():
     """INT8 ColBERT shape: one byte per element plus an fp32 scale per document and query
     token, the fp32 score per document."""
@@ -78,7 +90,9 @@ def test_int8_short_query_bytes_count_the_scales():
 @pytest.mark.parametrize("name,bound", [("colbert-b100k", "hbm"), ("csr-bf16", "hbm"),
                                         ("colbert-i8-b100k", "hbm"),
                                         ("colpali-bf16-b10k", "mfma"), ("colpali-i8-b10k", "mfma"),
-                                        ("batch-colbert-q8-b100k", "mfma"), ("csr-pq", "lds"),
+                                        ("batch-colbert-q8-b100k", "hbm"),
+                                        ("batch-colbert-q32-b100k", "mfma"), ("csr-pq", "lds"),
+                                        ("colbert-fp32", "hbm"), ("colpali-i8-b175k", "mfma"),
                                         ("train-csr", "hbm")])
 def test_bound_of_each_family(name, bound):
     assert bench.bound_of(bench.WORKLOADS[name]) == bound
