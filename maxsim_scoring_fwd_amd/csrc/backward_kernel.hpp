@@ -66,6 +66,7 @@ constexpr int DQ_ELEMS_PER_WG = 4096;  // dQ elements per workgroup (16-byte chu
 // 153 / 147 / 146 / 186 / 180 us, every instance at 8 waves per SIMD.
 constexpr int DQ_DOCS = 3;
 constexpr int DD_ROWS = 4;             // dD rows per lane with their gathers in flight
+constexpr int DD_PRE = 2;              // chosen query rows per dD row gathered ahead
 
 __device__ __forceinline__ void bwd_extent(const BwdArgs &a, int64_t b, int64_t &first,
                                            int64_t &len) {
@@ -370,45 +371,87 @@ __global__ void __launch_bounds__(BWD_THREADS) bwd_dd_kernel(BwdArgs a, int seg_
       if (QLDS && by_row) {
         for (int row = my_r; row < seg; row += rpi) emit(row, my_c);
       } else if (by_row) {
-        // The query is gathered through L2 (too large for LDS). DD_ROWS rows per lane at a
-        // time: their first query rows are gathered together (every load issued before any
-        // is waited for), then any further query rows in order, then the stores. gfx9 waits
-        // for a load together with every store issued before it, so row by row each gather
-        // would also wait for the previous row's store. Sums keep their order (0 + first +
-        // second ...), so results are unchanged. (With the query in LDS the grouping's
-        // registers cost more occupancy than it saves: CSR dD measured 2% slower.)
-        for (int row0 = my_r; row0 < seg; row0 += rpi * DD_ROWS) {
-          int e0[DD_ROWS], e1[DD_ROWS];
-          float acc[DD_ROWS][E];
+        // The query is gathered through L2 (too large for LDS), DD_ROWS rows per lane at a
+        // time, software-pipelined: the first DD_PRE chosen query rows of each row of the
+        // next batch (query row 0 where there are fewer) are gathered before this batch's
+        // stores are issued. gfx9 retires vector memory operations in order, so a gather
+        // issued after a store is waited for together with that store; issued before, it only
+        // waits for the stores of the batch before. Rows past the segment's end are clamped to
+        // its last row, so every batch issues the same number of gathers and stores (the
+        // compiler's waits then count exactly); a clamped lane writes that row's chunk again
+        // with the same bytes. Rows chosen more often gather the rest in order afterwards, and
+        // every row sums 0 + first + second ..., so results are unchanged. (With the query in
+        // LDS the batching's registers cost more occupancy than they save: CSR dD measured 2%
+        // slower.)
+        if (my_r < seg) {
+          const int step = rpi * DD_ROWS;
+          auto rows_of = [&](int row0, int (&rw)[DD_ROWS], int (&f0)[DD_ROWS], int (&f1)[DD_ROWS]) {
 #pragma unroll
-          for (int u = 0; u < DD_ROWS; u++) {
-            const int row = row0 + u * rpi;
-            e0[u] = row < seg ? off[row] : 0;
-            e1[u] = row < seg ? off[row + 1] : 0;
-          }
-#pragma unroll
-          for (int u = 0; u < DD_ROWS; u++) {
-            float x[E];
-            q_chunk(e0[u] < e1[u] ? idx[e0[u]] : 0, my_c, x);  // query row 0: a safe dummy
-            const bool has = e0[u] < e1[u];
-#pragma unroll
-            for (int k = 0; k < E; k++) acc[u][k] = 0.f + (has ? x[k] : 0.f);
-          }
-#pragma unroll
-          for (int u = 0; u < DD_ROWS; u++)
-            for (int e = e0[u] + 1; e < e1[u]; e++) {
-              float x[E];
-              q_chunk(idx[e], my_c, x);
-#pragma unroll
-              for (int k = 0; k < E; k++) acc[u][k] += x[k];
+            for (int u = 0; u < DD_ROWS; u++) {
+              const int row = row0 + u * rpi < seg ? row0 + u * rpi : seg - 1;
+              rw[u] = row;
+              f0[u] = off[row];
+              f1[u] = off[row + 1];
             }
+          };
+          auto gather_first = [&](const int (&f0)[DD_ROWS], const int (&f1)[DD_ROWS],
+                                  float (&xx)[DD_ROWS][DD_PRE][E]) {
 #pragma unroll
-          for (int u = 0; u < DD_ROWS; u++) {
-            const int row = row0 + u * rpi;
-            if (row < seg) {
+            for (int u = 0; u < DD_ROWS; u++)
+#pragma unroll
+              for (int p = 0; p < DD_PRE; p++)  // query row 0: a safe dummy
+                q_chunk(f0[u] + p < f1[u] ? idx[f0[u] + p] : 0, my_c, xx[u][p]);
+          };
+          int rw[DD_ROWS], f0[DD_ROWS], f1[DD_ROWS];
+          float xf[DD_ROWS][DD_PRE][E];
+          rows_of(my_r, rw, f0, f1);
+          gather_first(f0, f1, xf);
+          // Wait for the first batch here (vmcnt(0); expcnt and lgkmcnt unconstrained), so
+          // the loop is entered with no gather pending, as at its back-edge: otherwise the
+          // compiler's wait for a batch's gathers, merged over both ways into the loop, would
+          // also wait for the previous batch's stores.
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          for (int row0 = my_r;; row0 += step) {
+            const bool more = row0 + step < seg;
+            int nw[DD_ROWS], n0[DD_ROWS], n1[DD_ROWS];
+            float xn[DD_ROWS][DD_PRE][E];
+            rows_of(more ? row0 + step : row0, nw, n0, n1);  // the last batch gathers itself again
+            gather_first(n0, n1, xn);
+            float acc[DD_ROWS][E];
+#pragma unroll
+            for (int u = 0; u < DD_ROWS; u++) {
+#pragma unroll
+              for (int k = 0; k < E; k++) acc[u][k] = 0.f;
+#pragma unroll
+              for (int p = 0; p < DD_PRE; p++)
+#pragma unroll
+                for (int k = 0; k < E; k++) acc[u][k] += f0[u] + p < f1[u] ? xf[u][p][k] : 0.f;
+            }
+            // rows chosen by more than DD_PRE query tokens: the rest in order (rare)
+#pragma unroll
+            for (int u = 0; u < DD_ROWS; u++)
+              for (int e = f0[u] + DD_PRE; e < f1[u]; e++) {
+                float x[E];
+                q_chunk(idx[e], my_c, x);
+#pragma unroll
+                for (int k = 0; k < E; k++) acc[u][k] += x[k];
+              }
+#pragma unroll
+            for (int u = 0; u < DD_ROWS; u++) {
 #pragma unroll
               for (int k = 0; k < E; k++) acc[u][k] *= g;
-              store_chunk<OT, E, NT>(dst + ((int64_t)row * cpr + my_c) * 16, acc[u]);
+              store_chunk<OT, E, NT>(dst + ((int64_t)rw[u] * cpr + my_c) * 16, acc[u]);
+            }
+            if (!more) break;
+#pragma unroll
+            for (int u = 0; u < DD_ROWS; u++) {
+              rw[u] = nw[u];
+              f0[u] = n0[u];
+              f1[u] = n1[u];
+#pragma unroll
+              for (int p = 0; p < DD_PRE; p++)
+#pragma unroll
+                for (int k = 0; k < E; k++) xf[u][p][k] = xn[u][p][k];
             }
           }
         }
