@@ -138,6 +138,25 @@ def test_int8_csr_with_empty_docs():
     assert np.all(np.isneginf(tm[lens == 0])) and np.all(ta[lens == 0] == -1)
 
 
+@pytest.mark.parametrize("q_len", [32, 100])
+def test_int8_zero_tokens(q_len):
+    """Zero tokens quantise to all-zero codes with scale 0: their similarities are +0.
+    A document of zero tokens, zero tokens inside a document and a zero query token, on the
+    one-wave-per-document kernel (32 query tokens) and the query-tiled one (100)."""
+    say(f"case: int8 zero tokens q_len={q_len}")
+    c = gen.fixed_corpus(360 + q_len, 6, q_len, 70, 128, "i8")
+    c.D[1] = 0
+    c.d_scale[1] = 0.0
+    c.D[2, 5:40] = 0
+    c.d_scale[2, 5:40] = 0.0
+    c.Q[3] = 0
+    c.q_scale[3] = 0.0
+    check_i8(c, f"i8 zero tokens q={q_len}")
+    _, tm, ta = gpu_i8(c)
+    assert np.all(tm[1] == 0.0) and np.all(ta[1] == 0)  # all +0: the first token
+    assert np.all(tm[:, 3] >= 0.0)
+
+
 def test_int8_literal_int32_maxima_and_ties():
     """Unit scales: token maxima are the int32 maxima of the dot products; duplicated
     tokens create ties that must resolve to the lowest index."""
