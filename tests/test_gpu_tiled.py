@@ -20,8 +20,9 @@ def _lib():
     ms()
 
 
-# Up to 384 query tokens (256 at d=256 bf16) run 4 waves per workgroup, longer ones 8: the
-# lengths include both sides of each switch.
+# bf16 / fp16 queries of 65-256 tokens at d = 64 or 128 run on the document-stationary kernel
+# (queries in LDS); the rest split the query across 4 waves per workgroup up to 384 tokens
+# (256 at d=256 bf16) and 8 beyond: the lengths include both sides of each switch.
 LONG = [(q, d) for q in (65, 100, 128, 129, 255, 257, 384, 385, 512, 1000, 1024)
         for d in (64, 128, 256) if not (d == 256 and q > 512)]
 
@@ -68,9 +69,12 @@ def test_long_query_csr_ragged_and_empty():
     compare(got, oracle.maxsim_csr(c.Q, c.D, c.offsets, "bf16"), what="long CSR")
 
 
-def test_long_query_doc_lens():
-    say("case: long query with doc_lens")
-    c = gen.fixed_corpus(34, 10, 300, 200, 128, "bf16")
+@pytest.mark.parametrize("q_len", [100, 256, 300])
+def test_long_query_doc_lens(q_len):
+    """Padding past doc_lens holds large tokens that would win every max if read: on the
+    document-stationary kernel (100 and 256 query tokens) and the query-tiled one (300)."""
+    say(f"case: long query with doc_lens q_len={q_len}")
+    c = gen.fixed_corpus(34 + q_len, 10, q_len, 200, 128, "bf16")
     lens = np.array([0, 1, 15, 16, 17, 127, 128, 129, 199, 200], np.int32)
     D = c.D.copy()
     for b in range(10):
