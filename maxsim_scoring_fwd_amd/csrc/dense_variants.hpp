@@ -12,16 +12,17 @@ int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStre
   const size_t lds = q_lds + (LM == LOAD_STAGED ? DENSE_WAVES * stage_tile_bytes<KSB>() : 0);
   if (lds > di.max_lds) return MAXSIM_ERR_UNSUPPORTED;
   int bpc = blocks_per_cu((const void *)kern, DENSE_THREADS, lds);
-  // Fewer concurrent document streams read faster once each wave has a long contiguous
-  // range: bf16 / fp16 fixed documents of at least 32 KiB stream best from one workgroup
-  // per CU (one wave per SIMD; 100K ColBERT documents 0.489 -> 0.478 ms, 500K +2.7%, any
-  // query of 16-64 tokens alike), 16 KiB documents from two (+1.2-1.7%), provided every wave
-  // still gets at least 32 documents (10K documents are fastest uncapped). INT8, fp32,
-  // 512-byte rows, the query in LDS and the forward with argmax keep the full occupancy
-  // (measured no better or slower). MAXSIM_DENSE_WG_PER_CU=n forces a cap of n, 0 none.
+  // Fewer concurrent document streams read faster once each wave has a long range of
+  // documents: bf16 / fp16 fixed documents of at least 32 KiB stream best from one
+  // workgroup per CU (one wave per SIMD; 100K ColBERT documents 0.489 -> 0.478 ms, 500K
+  // +2.7%, any query of 16-64 tokens alike; with per-token outputs 0.556 -> 0.533 ms),
+  // 16 KiB documents from two (+1.2-1.7%), provided every wave still gets at least 32
+  // documents (10K documents are fastest uncapped). INT8, fp32, 512-byte rows and the query
+  // in LDS keep the full occupancy (measured no better or slower). MAXSIM_DENSE_WG_PER_CU=n
+  // forces a cap of n, 0 none.
   static const int wg_env = env_knob("MAXSIM_DENSE_WG_PER_CU", -1);
   int wg_cap = 0;
-  if constexpr ((DT == DT_BF16 || DT == DT_FP16) && !ARG && !QLDS && (KSB == 2 || KSB == 4)) {
+  if constexpr ((DT == DT_BF16 || DT == DT_FP16) && !QLDS && (KSB == 2 || KSB == 4)) {
     const int64_t doc_bytes = (int64_t)a.nd * KSB * 64;
     const int64_t per_wave = 32 * (int64_t)di.cus * DENSE_WAVES;  // documents at one WG per CU
     if (!a.offsets && doc_bytes >= 32768 && a.n_docs >= per_wave)
