@@ -43,8 +43,9 @@
 //  * INT8 storage (Flash-MaxSim abstract: INT8 x INT8 with per-token scales): the tile
 //    product is the exact int32 dot on the int8 matrix core (16x16x64, the same 64-byte
 //    chunks and operand layout), and each similarity is fl32(fl32(dot) * fl32(q_scale[i] *
-//    d_scale[j])) before the max, as in the query-tiled kernel. The scales of a lane's four
-//    rows travel with the tile's loads in the ring.
+//    d_scale[j])) before the max, as in the query-tiled kernel. The scale of a lane's tile row
+//    travels with the tile's loads in the ring, and the scale products of a tile come from
+//    one 4-block 16x16x1 fp32 MFMA (exact: one product plus zero, rounded once).
 //  * With ARG the kernel also writes each query token's maximum and the lowest
 //    document index reaching it (the argmax the Flash-MaxSim backward pass
 //    reuses): rows are folded in increasing order with a strict comparison, and
@@ -199,11 +200,12 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       }
     }
   }
-  // INT8: the scale of the lane's query column of each block (0 for padding)
-  float qs[I8 ? QB : 1];
+  // INT8: the B operand of the scale products (scale_products): the scale of column r16 of
+  // query block g (0 for padding and for blocks past QB)
+  float qsb = 0.f;
   if constexpr (I8) {
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++) qs[qb] = qb * 16 + r16 < q_len ? a.q_scale[qb * 16 + r16] : 0.f;
+    static_assert(!I8 || QB <= 4, "one scale-product MFMA covers four query blocks");
+    if (g < QB && g * 16 + r16 < q_len) qsb = a.q_scale[g * 16 + r16];
   }
   if constexpr (QLDS) {
     const int64_t per_row = RB / 16;
@@ -241,9 +243,9 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
 
   u32x4_t buf[P][KSB];
   Slot slot[P];
-  f32x4_t dsc[I8 ? P : 1];  // INT8: scales of the lane's rows 4g .. 4g + 3 of each slot's tile
+  float dsc[I8 ? P : 1];  // INT8: the scale of row r16 of each slot's tile
 
-  auto issue = [&](u32x4_t(&dst)[KSB], Slot &sl, f32x4_t &ds) {
+  auto issue = [&](u32x4_t(&dst)[KSB], Slot &sl, float &ds) {
     sl.valid = false;
     const char *base = a.Q;  // in-bounds dummy source for empty or exhausted slots
     const float *sbase = a.q_scale;  // INT8: the tile's first row scale, or a dummy
@@ -299,8 +301,7 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
     }
     if constexpr (I8) {
       // rows past the tile's last one take its scale, as their tokens duplicate it
-#pragma unroll
-      for (int r = 0; r < 4; r++) ds[r] = sbase[4 * g + r < last ? 4 * g + r : last];
+      ds = sbase[r16 < last ? r16 : last];
     } else {
       (void)ds;
     }
@@ -362,14 +363,15 @@ __global__ void __launch_bounds__(DENSE_THREADS) dense_maxsim_kernel(DenseArgs a
       }
       if constexpr (I8) {
         if (slot[p].last_blk) {
-          // fl32(fl32(dot) * fl32(q_scale * d_scale)) per similarity, then as below
+          // fl32(fl32(dot) * fl32(q_scale * d_scale)) per similarity, then as below; the
+          // scale products come from the matrix core, one MFMA per tile
           const int row0 = slot[p].tile * 16 + 4 * g;
+          const f32x16_t sp = scale_products(dsc[I8 ? p : 0], qsb);
 #pragma unroll
           for (int qb = 0; qb < QB; qb++) {
             float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; r++)
-              v[r] = __fmul_rn((float)acc[qb][r], __fmul_rn(qs[I8 ? qb : 0], dsc[I8 ? p : 0][r]));
+            for (int r = 0; r < 4; r++) v[r] = __fmul_rn((float)acc[qb][r], sp[4 * qb + r]);
             if constexpr (ARG) {
 #pragma unroll
               for (int r = 0; r < 4; r++)

@@ -32,6 +32,19 @@ __device__ __forceinline__ i32x4_t chunk_mfma_i8(u32x4_t a, u32x4_t b, i32x4_t c
                                                __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
 }
 
+// INT8 scale products on the matrix core. Four 16x16 blocks, K = 1: block k of the result,
+// lane l, element 4k + r, is a * b of lane (16k + 4 * (l / 16) + r) of the A operand and lane
+// (16k + l % 16) of the B operand: with A = a tile's 16 document-token scales (lane l: row
+// l % 16, the same in every block) and B = the scales of four query blocks (lane l: block
+// l / 16, column l % 16), element 4k + r of lane l is the scale product of accumulator
+// element r of query block k in that lane. One product plus zero per entry, rounded once:
+// fl32(q_scale * d_scale), bit for bit the rounded multiply.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16_t scale_products(float a, float b) {
+  const f32x16_t zero = {};
+  return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, zero, 0, 0, 0);
+}
+
 // Accumulator of one 16x16 tile: fp32, or int32 for INT8.
 template <bool INT> struct AccType { using type = f32x4_t; };
 template <> struct AccType<true> { using type = i32x4_t; };

@@ -47,18 +47,6 @@ namespace maxsim {
 constexpr int TILED_WAVES = 8;  // default waves per workgroup (query slices)
 constexpr int TILED_BLOCK_BYTES = 32 * 1024;
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-// Four 16x16 blocks, K = 1: block k of the result, lane l, element 4k + r, is
-// a * b of lane (16k + 4 * (l / 16) + r) of the A operand and lane (16k + l % 16) of the B
-// operand: with A = the tile's 16 document-token scales (lane l: row l % 16, the same in
-// every block) and B = the scales of four query blocks (lane l: block l / 16, column
-// l % 16), element 4k + r of lane l is the scale product of accumulator element r of
-// query block k in that lane. One product plus zero per entry, rounded once.
-__device__ __forceinline__ f32x16_t scale_products(float a, float b) {
-  const f32x16_t zero = {};
-  return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, zero, 0, 0, 0);
-}
 
 struct TiledArgs {
   const char *Q;
