@@ -56,9 +56,17 @@ int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStre
 // Staged loads need a power-of-two number of 16-byte pieces per row.
 template <int KSB> constexpr bool stageable() { return (KSB & (KSB - 1)) == 0; }
 
-// Tiles in flight per wave: 16-32 KiB of loads per wave (measured on the ColBERT shape,
-// depths 4 to 10 are within 1% of each other; 4 needs the fewest registers).
-template <int KSB> constexpr int default_depth() { return KSB <= 2 ? 8 : 4; }
+// Tiles in flight per wave. On the ColBERT shape depths 4 to 10 are within 1% of each other
+// and 4 needs the fewest registers. Short rows, measured at 100K documents of 128 tokens
+// against the former depth 8 (whose per-slot state spilled scalar registers): bf16 rows of
+// 128 bytes (d = 64) 83.0 -> 85.1% of HBM peak at depth 4, of 64 bytes (d = 32) 0.143 ->
+// 0.139 ms; INT8 rows of 128 bytes +0.7% at depth 4, of 64 bytes 0.156 -> 0.151-0.154 ms at
+// depth 6 (depth 4 slower there). fp32 short rows keep 8 (not measured).
+template <int DT, int KSB> constexpr int default_depth() {
+  if constexpr (DT == DT_I8) return KSB == 1 ? 6 : 4;
+  else if constexpr (DT == DT_FP32) return KSB <= 2 ? 8 : 4;
+  else return 4;
+}
 
 template <int DT, int KSB, int QB, bool QLDS, bool ARG>
 int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipStream_t st) {
@@ -89,18 +97,20 @@ int dense_with_depth(const DenseArgs &a, size_t lds, const DeviceInfo &di, hipSt
     if (depth == 10) return launch_dense<DT, KSB, QB, 10, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
     if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LOAD_STAGED, ARG>(a, lds, di, st);
   }
-  if constexpr (DT == DT_BF16 && KSB == 2 && QB == 2 && !ARG && !QLDS) {
-    // 128-byte rows (d = 64) with 32 query tokens: ring depth selectable for measurements
+  if constexpr ((DT == DT_BF16 || DT == DT_I8) && KSB <= 2 && QB == 2 && !ARG && !QLDS) {
+    // rows of 64 or 128 bytes with 32 query tokens: ring depth selectable for measurements
     static const int depth = env_knob("MAXSIM_DENSE_DEPTH", 0);
+    if (depth == 4) return launch_dense<DT, KSB, QB, 4, QLDS, LM, ARG>(a, lds, di, st);
+    if (depth == 6) return launch_dense<DT, KSB, QB, 6, QLDS, LM, ARG>(a, lds, di, st);
+    if (depth == 8) return launch_dense<DT, KSB, QB, 8, QLDS, LM, ARG>(a, lds, di, st);
     if (depth == 12) return launch_dense<DT, KSB, QB, 12, QLDS, LM, ARG>(a, lds, di, st);
-    if (depth == 16) return launch_dense<DT, KSB, QB, 16, QLDS, LM, ARG>(a, lds, di, st);
   }
   if constexpr (LM == LOAD_STAGED) {
     // Where Q already fills LDS, the transpose buffers may not fit: load directly.
     if (lds + DENSE_WAVES * stage_tile_bytes<KSB>() > di.max_lds)
-      return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LOAD_DIRECT, ARG>(a, lds, di, st);
+      return launch_dense<DT, KSB, QB, default_depth<DT, KSB>(), QLDS, LOAD_DIRECT, ARG>(a, lds, di, st);
   }
-  return launch_dense<DT, KSB, QB, default_depth<KSB>(), QLDS, LM, ARG>(a, lds, di, st);
+  return launch_dense<DT, KSB, QB, default_depth<DT, KSB>(), QLDS, LM, ARG>(a, lds, di, st);
 }
 
 template <int DT, int KSB, bool QLDS, bool ARG>
