@@ -17,9 +17,9 @@ int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStre
   // workgroup per CU (one wave per SIMD; 100K ColBERT documents 0.489 -> 0.478 ms, 500K
   // +2.7%, any query of 16-64 tokens alike; with per-token outputs 0.556 -> 0.533 ms),
   // 16 KiB documents from two (+1.2-1.7%), provided every wave still gets at least 32
-  // documents (10K documents are fastest uncapped). INT8, fp32, 512-byte rows and the query
-  // in LDS keep the full occupancy (measured no better or slower). MAXSIM_DENSE_WG_PER_CU=n
-  // forces a cap of n, 0 none.
+  // documents (10K documents are fastest uncapped). fp32, 512-byte rows and the query in LDS
+  // keep the full occupancy (measured no better or slower); INT8 below. MAXSIM_DENSE_WG_PER_CU
+  // =n forces a cap of n, 0 none.
   static const int wg_env = env_knob("MAXSIM_DENSE_WG_PER_CU", -1);
   int wg_cap = 0;
   if constexpr ((DT == DT_BF16 || DT == DT_FP16) && !QLDS && (KSB == 2 || KSB == 4)) {
@@ -29,6 +29,11 @@ int launch_dense(const DenseArgs &a, size_t q_lds, const DeviceInfo &di, hipStre
       wg_cap = 1;
     else if (!a.offsets && doc_bytes >= 16384 && a.n_docs >= 2 * per_wave)
       wg_cap = 2;
+  }
+  if constexpr (DT == DT_I8 && KSB == 2 && !QLDS) {
+    // INT8 rows of 128 bytes (depth 4, up to 5 workgroups per CU): three per CU, 80.5-80.8
+    // -> 82.0-82.2% of HBM peak at 100K documents (one per CU 61%, two unsteady)
+    if (!a.offsets && a.n_docs >= 3 * 32 * (int64_t)di.cus * DENSE_WAVES) wg_cap = 3;
   }
   if (wg_env >= 0) wg_cap = wg_env;
   if (wg_cap > 0 && wg_cap < bpc) bpc = wg_cap;
