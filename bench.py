@@ -630,8 +630,12 @@ def calib_suite():
 
     out = {"device": torch.cuda.get_device_name(0)}
     buf = torch.ones(1 << 30, dtype=torch.int32, device=dev)
-    t, _ = med(lambda: ms.calib_read(buf, usink))
-    out["stream_read_GBps"] = round(buf.numel() * 4 / (t * 1e-3) / 1e9, 1)
+    # one workgroup of 4 waves per CU, and as many as fit: the faster is the ceiling
+    for n, key in ((1, "stream_read_1wg_per_cu_GBps"), (0, "stream_read_full_occupancy_GBps")):
+        t, _ = med(lambda: ms.calib_read(buf, usink, wgs_per_cu=n))
+        out[key] = round(buf.numel() * 4 / (t * 1e-3) / 1e9, 1)
+    out["stream_read_GBps"] = max(out["stream_read_1wg_per_cu_GBps"],
+                                  out["stream_read_full_occupancy_GBps"])
     t, _ = med(lambda: ms.calib_write(buf))
     out["stream_write_GBps"] = round(buf.numel() * 4 / (t * 1e-3) / 1e9, 1)
     del buf
@@ -796,24 +800,32 @@ def main():
             torch.cuda.synchronize()
             return sorted(s.elapsed_time(e) for s, e in zip(cs, ce))[5]
 
-        stream_gbs = buf.numel() * 4 / (median_ms(lambda: ms.calib_read(buf, sink)) * 1e-3) / 1e9
+        # the stream read with one workgroup of 4 waves per CU and with as many as fit: the
+        # faster of the two is the ceiling
+        reads = {n: buf.numel() * 4 / (median_ms(lambda: ms.calib_read(buf, sink, wgs_per_cu=n))
+                                       * 1e-3) / 1e9 for n in (1, 0)}
+        stream_gbs = max(reads.values())
         context["stream_read_GBps"] = round(stream_gbs, 1)
+        context["stream_read_GBps_by_launch"] = {"1_wg_per_cu": round(reads[1], 1),
+                                                 "full_occupancy": round(reads[0], 1)}
         if flush and bound == "hbm" and w["path"] != "train":
             # a corpus this small is dominated by launch and ramp-up: the same stream read
             # over the same number of bytes, caches flushed the same way, is its ceiling
             n_small = min(footprint // 16 * 4, buf.numel())
             small = buf[:n_small]
-            ts = []
-            for i in range(13):
-                scratch.zero_()
-                cs, ce = TimingEvent(), TimingEvent()
-                cs.record(stream)
-                ms.calib_read(small, sink)
-                ce.record(stream)
-                torch.cuda.synchronize()
-                if i >= 3:
-                    ts.append(cs.elapsed_time(ce))
-            small_gbs = n_small * 4 / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
+            small_gbs = 0.0
+            for n in (1, 0):  # the faster of the two launch shapes, as above
+                ts = []
+                for i in range(13):
+                    scratch.zero_()
+                    cs, ce = TimingEvent(), TimingEvent()
+                    cs.record(stream)
+                    ms.calib_read(small, sink, wgs_per_cu=n)
+                    ce.record(stream)
+                    torch.cuda.synchronize()
+                    if i >= 3:
+                        ts.append(cs.elapsed_time(ce))
+                small_gbs = max(small_gbs, n_small * 4 / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9)
             context["stream_read_same_bytes_GBps"] = round(small_gbs, 1)
             context["frac_of_stream_read_same_bytes"] = round(achieved / small_gbs, 4)
             log(f"stream read of the same {n_small * 4} bytes, caches flushed: {small_gbs:.0f} GB/s")

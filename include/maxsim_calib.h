@@ -2,10 +2,10 @@
  * Measurement helpers shipped with libmaxsim (not part of the scoring path).
  *
  * maxsim_calib_read streams `bytes` from `src` with non-temporal 128-bit loads (each
- * wave reading whole 16 KiB blocks) and writes one
- * word per workgroup to `sink` (so the reads cannot be optimised away): its
- * duration gives the achievable HBM read bandwidth of the device, the ceiling a
- * memory-bound scoring kernel can approach.
+ * wave reading whole 16 KiB blocks, `wgs_per_cu` workgroups of 4 waves per CU, <= 0 or
+ * more than fit: as many as fit) and writes one word per workgroup to `sink` (so the
+ * reads cannot be optimised away): its duration gives the achievable HBM read bandwidth
+ * of the device, the ceiling a memory-bound scoring kernel can approach.
  * maxsim_calib_copy copies `bytes` from src to dst with 128-bit loads and stores:
  * a plain copy of known size, used to scale hardware traffic counters.
  *
@@ -24,7 +24,7 @@
 extern "C" {
 #endif
 
-int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int maxsim_calib_read(const void *src, size_t bytes, int wgs_per_cu, uint32_t *sink, void *stream);
 /* Streams `bytes` of a fixed pattern into dst with 128-bit stores (each wave writing whole
  * 16 KiB blocks, one workgroup per CU): the achievable HBM write bandwidth, the ceiling
  * of a kernel that mostly writes (the backward's dD). dst 16-byte aligned, bytes % 16 == 0. */

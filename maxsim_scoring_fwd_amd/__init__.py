@@ -430,7 +430,7 @@ def _calib_lib():
     L = lib()
     if not getattr(L, "_calib_bound", False):
         vp = ctypes.c_void_p
-        L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
         L.maxsim_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
         L.maxsim_calib_write.argtypes = [vp, ctypes.c_size_t, vp]
         L.maxsim_calib_write.restype = ctypes.c_int
@@ -448,10 +448,12 @@ def _calib_lib():
     return L
 
 
-def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
-    """Stream-read every byte of src (achievable read bandwidth); sink: >= 65536 words."""
+def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None, wgs_per_cu: int = 1):
+    """Stream-read every byte of src (achievable read bandwidth) with wgs_per_cu workgroups
+    of 4 waves per CU (0: as many as fit); sink: >= 65536 words."""
     _check(_calib_lib().maxsim_calib_read(_dev(src, "src"), src.numel() * src.element_size(),
-                                          _dev(sink, "sink"), _stream(stream)), "maxsim_calib_read")
+                                          int(wgs_per_cu), _dev(sink, "sink"), _stream(stream)),
+           "maxsim_calib_read")
 
 
 def calib_write(dst: torch.Tensor, stream=None):

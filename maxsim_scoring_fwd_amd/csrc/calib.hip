@@ -15,7 +15,8 @@ using maxsim::u32x4_t;
 constexpr int CAL_THREADS = 256;
 
 // Each wave reads whole blocks of LOADS KiB: LOADS loads of 1 KiB in flight per wave,
-// every load instruction covering 1 KiB of contiguous memory.
+// every load instruction covering 1 KiB of contiguous memory, the blocks dealt to the
+// waves in turn.
 template <bool NT, int LOADS>
 __global__ void __launch_bounds__(CAL_THREADS) calib_read_kernel(const u32x4_t *src, size_t n16,
                                                                  uint32_t *sink) {
@@ -76,7 +77,8 @@ __global__ void __launch_bounds__(CAL_THREADS) calib_copy_kernel(const u32x4_t *
 
 }  // namespace
 
-extern "C" int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+extern "C" int maxsim_calib_read(const void *src, size_t bytes, int wgs_per_cu, uint32_t *sink,
+                                 void *stream) {
   if (!src || !sink) return MAXSIM_ERR_NULL;
   if (bytes % 16 || !maxsim::aligned(src, 16)) return MAXSIM_ERR_ALIGN;
   maxsim::DeviceInfo di;
@@ -87,7 +89,10 @@ extern "C" int maxsim_calib_read(const void *src, size_t bytes, uint32_t *sink, 
   auto kern = nt ? calib_read_kernel<true, 16> : calib_read_kernel<false, 16>;
   if (loads == 8) kern = nt ? calib_read_kernel<true, 8> : calib_read_kernel<false, 8>;
   if (loads == 32) kern = nt ? calib_read_kernel<true, 32> : calib_read_kernel<false, 32>;
-  const int bpc = maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
+  // 4 GiB on MI355X: one workgroup per CU (one wave per SIMD) 7.09 TB/s, two 6.94, as many
+  // as fit (8) 6.82; fewer waves keep longer runs of each DRAM page open
+  const int occ = maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
+  const int bpc = wgs_per_cu > 0 && wgs_per_cu < occ ? wgs_per_cu : occ;
   hipLaunchKernelGGL(kern, dim3(bpc * di.cus), dim3(CAL_THREADS), 0, (hipStream_t)stream,
                      (const u32x4_t *)src, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
