@@ -223,8 +223,9 @@ def intensity(w) -> float:
 
 def bound_of(w):
     """The roofline that bounds the scoring kernel: HBM below the ridge point (peak
-    operations per second over 8 TB/s), the matrix core above it; the training step's dD
-    kernel writes a gradient row per token (HBM), PQ lookups read LDS."""
+    operations per second over 8 TB/s), the matrix core above it; PQ lookups read LDS. A
+    training step's bound is its longest launch's (train_roofline, once timed); before
+    that, its dD kernel's, which writes a gradient row per token (HBM)."""
     if w["path"] == "train":
         return "hbm"
     if w["path"] == "pq":
@@ -378,6 +379,24 @@ def train_dd_bytes(w, inp):
     return b
 
 
+def train_roofline(w, inp, name):
+    """Roofline of one launch of the training step, (bound, work per launch, unit, kernel
+    family): the forward with per-token argmax by its intensity (the matrix core above the
+    ridge, else the bytes it reads and writes: documents, query, scores, per-token maxima and
+    argmax), dQ by the rows it gathers, dD by the rows it writes."""
+    n_tok, q, d, B, e = inp["n_tokens"], w["q_len"], w["d"], w["B"], esize(w["dtype"])
+    off = (B + 1) * 8 if inp["offsets"] is not None else 0
+    if name == "maxsim_argmax":
+        fam = "dense" if short_query(w) else "tiled"
+        ridge = MFMA_PEAK_TFLOPS[w["dtype"]] * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if intensity(w) > ridge:
+            return "mfma", 2 * q * n_tok * d, "TFLOP/s", fam
+        return "hbm", n_tok * d * e + q * d * e + B * 4 + B * q * 8 + off, "GB/s", fam
+    if name == "backward_dq":
+        return "hbm", B * q * (d * e + 4) + B * 4 + q * d * e * 2, "GB/s", "train"
+    return "hbm", train_dd_bytes(w, inp), "GB/s", "train"
+
+
 def hbm_bytes(w, inp):
     """Bytes every document token costs in HBM (for context on mfma / lds-bound paths)."""
     if w["path"] == "pq":
@@ -394,7 +413,7 @@ def hbm_bytes(w, inp):
 
 def launches(ms, w, inp, out):
     """The kernel launches of one step, as (name, callable). The roofline is taken on the
-    dominant one: the scoring kernel, else the last launch."""
+    dominant one: the scoring kernel; in a training step the longest of its launches."""
     steps = _scoring_launches(ms, w, inp, out)
     if w.get("topk"):
         n_q = w.get("n_q", 1)
@@ -412,7 +431,7 @@ def launches(ms, w, inp, out):
 
 def dominant_index(steps):
     names = [n for n, _ in steps]
-    for n in ("maxsim", "maxsim_batch", "maxsim_i8", "pq_score", "backward_dd"):
+    for n in ("maxsim", "maxsim_batch", "maxsim_i8", "pq_score"):
         if n in names:
             return names.index(n)
     return len(steps) - 1
@@ -537,13 +556,15 @@ def cpu_baseline(w, budget_s: float):
 # convert, the product with its scale product (the scale products themselves run on the
 # matrix core) and half a three-way max; bf16 / fp16 half a three-way max.
 VALU_PER_SIMILARITY = {"i8": 2.5, "bf16": 0.5, "fp16": 0.5}
+# the forward with per-token argmax (bf16 / fp16): a compare and two selects per similarity
+VALU_PER_SIMILARITY_ARGMAX = 3.0
 # matrix-core cycles per 16 x 16 tile and query block relative to the dot products alone:
 # INT8 adds a 32-cycle 16x16x1 4-block fp32 MFMA (scale products) per four 16-cycle int8
 # ones at d = 128
 MFMA_EXTRA = {"i8": 1.25, "bf16": 1.0, "fp16": 1.0}
 
 
-def compute_ceilings(ms, w, achieved, stream, median_ms):
+def compute_ceilings(ms, w, achieved, stream, median_ms, valu_per_sim=None):
     """Measured ceilings of a matrix-core-bound workload, at the query-tiled kernels'
     occupancy (two waves per SIMD): the sustained MFMA rate of its dtype and the sustained
     vector-ALU rate, each alone, and two bounds for both together, from the workload's MFMA
@@ -564,7 +585,8 @@ def compute_ceilings(ms, w, achieved, stream, median_ms):
     # one VALU instruction per lane per FMA (2 FLOP): lane-instructions per second
     lane_instr = valu * 1e12 / 2
     ops_per_sim = 2 * w["d"]
-    valu_bound = lane_instr / VALU_PER_SIMILARITY[w["dtype"]] * ops_per_sim / 1e12
+    vps = valu_per_sim if valu_per_sim is not None else VALU_PER_SIMILARITY[w["dtype"]]
+    valu_bound = lane_instr / vps * ops_per_sim / 1e12
     mfma_bound = mfma / MFMA_EXTRA[w["dtype"]]
     additive = 1.0 / (1.0 / mfma_bound + 1.0 / valu_bound)
     # exposed share of the smaller time in the balanced calibration: the launch's MFMA-only
@@ -580,7 +602,7 @@ def compute_ceilings(ms, w, achieved, stream, median_ms):
     return {"mfma_sustained_TOPs_2w": round(mfma, 1),
             "frac_of_mfma_sustained": round(achieved / mfma, 4),
             "valu_fp32_TFLOPs_2w": round(valu, 1),
-            "valu_per_similarity": VALU_PER_SIMILARITY[w["dtype"]],
+            "valu_per_similarity": vps,
             "valu_bound_TOPs": round(valu_bound, 1),
             "mfma_plus_valu_bound_TOPs": round(additive, 1),
             "frac_of_mfma_plus_valu_bound": round(achieved / additive, 4),
@@ -752,7 +774,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [e[0].elapsed_time(e[-1]) for e in evs]
-    di = dominant_index(steps_fns)
+    per_launch = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / len(evs)
+                  for j in range(len(steps_fns))]
+    family = kernel_family(w)
+    bound = bound_of(w)
+    if w["path"] == "train":
+        # the training step's launches differ by shape: the longest one is the dominant kernel
+        di = max(range(len(steps_fns)), key=lambda j: per_launch[j])
+        bound, work, rate_unit, family = train_roofline(w, inp, steps_fns[di][0])
+    else:
+        di = dominant_index(steps_fns)
     dom_ms = [e[di].elapsed_time(e[di + 1]) for e in evs]  # the dominant kernel
     avg_step, avg_dom = sum(step_ms) / len(step_ms), sum(dom_ms) / len(dom_ms)
     log(f"timed {args.steps} steps: wall {wall * 1e3 / args.steps:.4f} ms/step, step events avg "
@@ -763,7 +794,6 @@ def main():
     else:
         value, ms_per_step = n_q * w["B"] * args.steps / wall, wall * 1e3 / args.steps
 
-    bound = bound_of(w)
     if bound == "mfma":
         achieved = work / (avg_dom * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[w["dtype"]]
@@ -774,14 +804,19 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload)
-        if rec and rec.get("kernel_hash") == kernel_hash(kernel_family(w)):
+        # a reading applies to the kernel family it was taken on (a training step's reading
+        # is of its dD kernel, hashed as the backward's family)
+        if rec and rec.get("kernel_hash") == kernel_hash(family):
             traffic = rec.get("bytes_per_launch")
 
     context = {"dominant_kernel": steps_fns[di][0], "kernel_ms_avg": round(avg_dom, 5),
                "kernel_ms_min": round(min(dom_ms), 5), "work_per_launch": work,
                "hbm_bytes_per_step": footprint,
                "hbm_GBps": round(footprint / (avg_step * 1e-3) / 1e9, 1),
-               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash(kernel_family(w))}
+               "caches_flushed_between_steps": flush, "kernel_hash": kernel_hash(family)}
+    if len(steps_fns) > 1:
+        context["kernel_ms_per_launch"] = {n: round(per_launch[j], 5)
+                                           for j, (n, _) in enumerate(steps_fns)}
     if w.get("pool") and w["pool"] < w["B"]:
         context["pool"] = f"{w['pool']} distinct documents repeated to {w['B']}"
     if not args.no_calib:
@@ -829,11 +864,14 @@ def main():
             context["stream_read_same_bytes_GBps"] = round(small_gbs, 1)
             context["frac_of_stream_read_same_bytes"] = round(achieved / small_gbs, 4)
             log(f"stream read of the same {n_small * 4} bytes, caches flushed: {small_gbs:.0f} GB/s")
-        if bound == "mfma" and w["dtype"] != "fp32":
+        if bound == "mfma" and w["dtype"] != "fp32" and w["path"] != "train":
             context.update(compute_ceilings(ms, w, achieved, stream, median_ms))
         if bound == "lds":
             context.update(lds_ceilings(ms, achieved, median_ms))
-        if w["path"] == "train":
+        if bound == "mfma" and w["path"] == "train":
+            context.update(compute_ceilings(ms, w, achieved, stream, median_ms,
+                                            valu_per_sim=VALU_PER_SIMILARITY_ARGMAX))
+        elif w["path"] == "train" and steps_fns[di][0] == "backward_dd":
             # the dD kernel mostly writes: its ceiling is the streaming-write rate
             wr_gbs = buf.numel() * 4 / (median_ms(lambda: ms.calib_write(buf)) * 1e-3) / 1e9
             context["stream_write_GBps"] = round(wr_gbs, 1)
@@ -868,9 +906,6 @@ def main():
         cfg["n_q"] = n_q
     if w.get("topk"):
         cfg["topk"] = w["topk"]
-        context["kernel_ms_per_launch"] = {
-            n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / len(evs), 5)
-            for j, (n, _) in enumerate(steps_fns)}
     if w["path"] == "train":
         cfg["step"] = ("scores with per-token argmax, then dQ and dD of sum_b g_b score_b "
                        f"(g_b ~ N(0,1), gradients in {w['dtype']})")

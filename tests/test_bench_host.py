@@ -56,6 +56,25 @@ def test_training_dd_algorithmic_bytes():
     assert b == 3_290_008_192
 
 
+def test_training_step_roofline_per_launch():
+    """A training step's roofline follows the launch that dominates it. The ColPali forward
+    with argmax (1024 FLOP per document byte) is matrix-core work on the query-tiled kernel;
+    the ColBERT one (32 FLOP per byte) reads the documents and writes the scores and the
+    per-token maxima and argmax; dD writes the gradient rows."""
+    w = bench.WORKLOADS["train-colpali-b10k"]
+    inp = _inputs(w)
+    bound, work, unit, fam = bench.train_roofline(w, inp, "maxsim_argmax")
+    assert (bound, unit, fam) == ("mfma", "TFLOP/s", "tiled")
+    assert work == 2 * 1024 * 10_000 * 1024 * 128
+    w = bench.WORKLOADS["train-colbert-b100k"]
+    inp = _inputs(w)
+    bound, work, unit, fam = bench.train_roofline(w, inp, "maxsim_argmax")
+    assert (bound, unit, fam) == ("hbm", "GB/s", "dense")
+    assert work == 100_000 * 128 * 128 * 2 + 32 * 128 * 2 + 100_000 * 4 + 100_000 * 32 * 8
+    assert bench.train_roofline(w, inp, "backward_dd") == ("hbm", bench.train_dd_bytes(w, inp),
+                                                           "GB/s", "train")
+
+
 def test_matrix_core_work_counts_every_query():
     w = bench.WORKLOADS["batch-colbert-q32-b100k"]
     work, unit = bench.work_per_launch(w, _inputs(w))
