@@ -25,10 +25,12 @@ extern "C" {
 #endif
 
 int maxsim_calib_read(const void *src, size_t bytes, int wgs_per_cu, uint32_t *sink, void *stream);
-/* Streams `bytes` of a fixed pattern into dst with 128-bit stores (each wave writing whole
- * 16 KiB blocks, one workgroup per CU): the achievable HBM write bandwidth, the ceiling
- * of a kernel that mostly writes (the backward's dD). dst 16-byte aligned, bytes % 16 == 0. */
-int maxsim_calib_write(void *dst, size_t bytes, void *stream);
+/* Streams `bytes` of a fixed pattern into dst with 128-bit stores, each wave writing whole
+ * 16 KiB blocks, `wgs_per_cu` workgroups of 4 waves per CU (<= 0 or more than fit: as many
+ * as fit); contig != 0 gives each wave one contiguous range of blocks, else the blocks go
+ * to the waves in turn: the achievable HBM write bandwidth, the ceiling of a kernel that
+ * mostly writes (the backward's dD). dst 16-byte aligned, bytes % 16 == 0. */
+int maxsim_calib_write(void *dst, size_t bytes, int wgs_per_cu, int contig, void *stream);
 int maxsim_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /*

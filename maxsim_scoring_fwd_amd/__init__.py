@@ -432,7 +432,7 @@ def _calib_lib():
         vp = ctypes.c_void_p
         L.maxsim_calib_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
         L.maxsim_calib_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
-        L.maxsim_calib_write.argtypes = [vp, ctypes.c_size_t, vp]
+        L.maxsim_calib_write.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
         L.maxsim_calib_write.restype = ctypes.c_int
         L.maxsim_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
         L.maxsim_calib_read.restype = ctypes.c_int
@@ -456,10 +456,13 @@ def calib_read(src: torch.Tensor, sink: torch.Tensor, stream=None, wgs_per_cu: i
            "maxsim_calib_read")
 
 
-def calib_write(dst: torch.Tensor, stream=None):
-    """Stream a fixed pattern into every byte of dst (achievable write bandwidth)."""
+def calib_write(dst: torch.Tensor, stream=None, wgs_per_cu: int = 2, contig: bool = True):
+    """Stream a fixed pattern into every byte of dst (achievable write bandwidth) with
+    wgs_per_cu workgroups of 4 waves per CU (0: as many as fit), each wave writing one
+    contiguous range (contig) or blocks dealt in turn."""
     _check(_calib_lib().maxsim_calib_write(_dev(dst, "dst"), dst.numel() * dst.element_size(),
-                                           _stream(stream)), "maxsim_calib_write")
+                                           int(wgs_per_cu), int(bool(contig)), _stream(stream)),
+           "maxsim_calib_write")
 
 
 def calib_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

@@ -48,14 +48,21 @@ __global__ void __launch_bounds__(CAL_THREADS) calib_read_kernel(const u32x4_t *
 // store instruction covering 1 KiB of contiguous memory (the pattern of a streaming writer).
 template <bool NT>
 __global__ void __launch_bounds__(CAL_THREADS) calib_write_kernel(u32x4_t *dst, size_t n16,
-                                                                  uint32_t pattern) {
+                                                                  uint32_t pattern, int contig) {
   constexpr size_t BLOCK16 = 64 * 16;
   const int lane = threadIdx.x & 63;
   const size_t wave = (size_t)blockIdx.x * (CAL_THREADS / 64) + (threadIdx.x >> 6);
   const size_t nwaves = (size_t)gridDim.x * (CAL_THREADS / 64);
   const size_t nblk = n16 / BLOCK16;
   const u32x4_t v = {pattern, pattern ^ 1u, pattern ^ 2u, pattern ^ 3u};
-  for (size_t b = wave; b < nblk; b += nwaves) {
+  // blocks dealt to the waves in turn, or with contig one contiguous range per wave
+  size_t b0 = wave, b1 = nblk, bstep = nwaves;
+  if (contig) {
+    b0 = nblk * wave / nwaves;
+    b1 = nblk * (wave + 1) / nwaves;
+    bstep = 1;
+  }
+  for (size_t b = b0; b < b1; b += bstep) {
     u32x4_t *p = dst + b * BLOCK16 + lane;
 #pragma unroll
     for (int u = 0; u < 16; u++) {
@@ -98,20 +105,21 @@ extern "C" int maxsim_calib_read(const void *src, size_t bytes, int wgs_per_cu, 
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
-extern "C" int maxsim_calib_write(void *dst, size_t bytes, void *stream) {
+extern "C" int maxsim_calib_write(void *dst, size_t bytes, int wgs_per_cu, int contig,
+                                  void *stream) {
   if (!dst) return MAXSIM_ERR_NULL;
   if (bytes % 16 || !maxsim::aligned(dst, 16)) return MAXSIM_ERR_ALIGN;
   maxsim::DeviceInfo di;
   int rc = maxsim::current_device(di);
   if (rc != MAXSIM_OK) return rc;
-  // Ordinary stores from one workgroup per CU measured fastest on MI355X (5.6 TB/s, against
-  // 4.6-5.2 TB/s for non-temporal stores or higher occupancy); knobs select the others.
+  // 4 GiB on MI355X, ordinary 16-byte stores: one contiguous range per wave at two
+  // workgroups per CU 5.86 TB/s, blocks in turn at one 5.58; non-temporal stores 5.03-5.47
   static const int nt = maxsim::env_knob("MAXSIM_CALIB_WRITE_NT", 0);
-  static const int wpc = maxsim::env_knob("MAXSIM_CALIB_WRITE_WGS", 1);
   auto kern = nt ? calib_write_kernel<true> : calib_write_kernel<false>;
-  const int bpc = wpc > 0 ? wpc : maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
+  const int occ = maxsim::blocks_per_cu((const void *)kern, CAL_THREADS, 0);
+  const int bpc = wgs_per_cu > 0 && wgs_per_cu < occ ? wgs_per_cu : occ;
   hipLaunchKernelGGL(kern, dim3(bpc * di.cus), dim3(CAL_THREADS), 0, (hipStream_t)stream,
-                     (u32x4_t *)dst, bytes / 16, 0x3f800000u);
+                     (u32x4_t *)dst, bytes / 16, 0x3f800000u, contig);
   return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_LAUNCH;
 }
 
